@@ -1,0 +1,278 @@
+"""Throughput of the MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_fp8]
+                    [--no-cpu-baseline] [--stages/--no-stages]
+
+One step = one whole layer forward (route -> dispatch -> 1x128 FP8 quant -> grouped
+GEMM1 + SwiGLU + requant -> grouped GEMM2 -> combine) through the C ABI call
+moe_layer_fwd on seeded synthetic inputs already resident in HBM.  Prints one JSON
+line.  `value` is the algorithmic FLOP rate of the layer (router + both expert GEMMs,
+unpadded rows) in TFLOP/s; tokens/s is reported beside it.  The roofline entry is for
+the dominant kernel (the grouped GEMM1), timed with HIP events on the launch stream.
+The CPU baseline times the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_layer(w: synth.Workload, dev):
+    import fp8_grouped_gemm_amd as M
+    inp = synth.layer_inputs(w, device=dev)
+    weights = {}
+    if w.route == "score":
+        weights["w_router"], weights["bias"] = inp["w_router"], inp["bias"]
+    if w.mode == "fp8":
+        weights["w13"], weights["s13"] = M.moe_quant_weight_fp8(inp["w13"])
+        weights["w2"], weights["s2"] = M.moe_quant_weight_fp8(inp["w2"])
+    elif w.mode == "w4a16":
+        weights["w13"], weights["s13"] = M.moe_quant_weight_int4(inp["w13"])
+        weights["w2"], weights["s2"] = M.moe_quant_weight_int4(inp["w2"])
+    else:
+        weights["w13"], weights["w2"] = inp["w13"], inp["w2"]
+    return inp, weights
+
+
+def gemm_bytes_flops(w: synth.Workload, counts: np.ndarray):
+    """Algorithmic work of the two expert GEMMs from the routed counts (unpadded rows):
+    FLOPs 2*M*N*K each; bytes = weights (+ scales) of touched experts + activations in +
+    outputs, each once."""
+    R = int(counts.sum())
+    touched = int(np.sum(counts > 0))
+    d, I = w.d, w.I
+    if w.mode == "fp8":
+        wb13 = 2 * I * d + (2 * I // 128) * (d // 128) * 4
+        wb2 = d * I + (d // 128) * (I // 128) * 4
+        a1 = w.T * d + w.T * (d // 128) * 4               # token codes + scales
+        h = R * I + R * (I // 128) * 4                     # requantised h
+        o = R * d * 2                                      # bf16 expert rows
+    elif w.mode == "w4a16":
+        wb13 = 2 * I * d // 2 + 2 * I * (d // 128) * 4
+        wb2 = d * I // 2 + d * (I // 128) * 4
+        a1 = w.T * d * 2
+        h = R * I * 2
+        o = R * d * 2
+    else:
+        wb13, wb2 = 2 * I * d * 4, d * I * 4
+        a1, h, o = w.T * d * 4, R * I * 4, R * d * 4
+    f1 = 2.0 * R * (2 * I) * d
+    f2 = 2.0 * R * d * I
+    b1 = touched * wb13 + a1 + h
+    b2 = touched * wb2 + h + o
+    return {"gemm1_flops": f1, "gemm2_flops": f2, "gemm1_bytes": b1, "gemm2_bytes": b2,
+            "rows": R, "touched": touched}
+
+
+def layer_flops_bytes(w: synth.Workload, counts: np.ndarray):
+    g = gemm_bytes_flops(w, counts)
+    router = 2.0 * w.T * w.E * w.d if w.route == "score" else 0.0
+    act = 4 if w.mode == "fp32" else 2
+    touched_w = g["gemm1_bytes"] + g["gemm2_bytes"] - 2 * (g["rows"] * w.I) - \
+        (g["rows"] * w.d * act)
+    wr = w.E * w.d * act if w.route == "score" else 0
+    total_bytes = touched_w + w.T * w.d * act * 2 + wr     # weights + x + y + router
+    return router + g["gemm1_flops"] + g["gemm2_flops"], total_bytes, g
+
+
+# ------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w: synth.Workload, inp: dict, n_experts: int = 8):
+    """Time the fp64 oracle on a bounded sample: routing + dispatch of the whole batch,
+    then the expert FFN (dequantise, GEMM1, SwiGLU, requant, GEMM2) of the rows routed
+    to ``n_experts`` experts.  Weight quantisation (offline) is outside the timer."""
+    import oracle as O
+    from oracle import codecs as OC
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x = inp["x"].float().cpu().numpy()
+    wr = inp["w_router"].float().cpu().numpy()
+    b = inp["bias"].cpu().numpy()
+    t0 = time.perf_counter()
+    logits = O.router_logits(x, wr)
+    idx, gw = O.topk_route(logits.astype(np.float32), b, w.k)
+    counts, offsets, ros, sor = O.dispatch(idx, w.E, w.m_align)
+    qx, sx = OC.quant_fp8_act(x)
+    t_route = time.perf_counter() - t0
+    order = np.argsort(-counts, kind="stable")
+    experts = [int(e) for e in order[:n_experts // 2]] + \
+              [int(e) for e in order[len(order) // 2:len(order) // 2 + n_experts - n_experts // 2]]
+    flops = 2.0 * w.T * w.E * w.d
+    t_exp = 0.0
+    rows_done = 0
+    for e in experts:
+        w13 = inp["w13"][e:e + 1].cpu().numpy()
+        w2 = inp["w2"][e:e + 1].cpu().numpy()
+        q13, s13 = OC.quant_fp8_weight(w13)
+        q2, s2 = OC.quant_fp8_weight(w2)
+        rows = np.arange(offsets[e], offsets[e + 1])
+        slots = sor[rows]
+        slots = slots[slots >= 0]
+        toks = slots // w.k
+        t0 = time.perf_counter()
+        a = OC.dequant_fp8_act(qx[toks], sx[toks])
+        W13 = OC.dequant_fp8_weight(q13, s13)[0]
+        W2 = OC.dequant_fp8_weight(q2, s2)[0]
+        gu = a @ W13.T
+        h = O.swiglu(gu[:, :w.I], gu[:, w.I:])
+        qh, sh = OC.quant_fp8_act(h.astype(np.float32))
+        _ = OC.dequant_fp8_act(qh, sh) @ W2.T
+        t_exp += time.perf_counter() - t0
+        rows_done += len(toks)
+        flops += 2.0 * len(toks) * (2 * w.I * w.d + w.d * w.I)
+    total = t_route + t_exp
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle: routing+dispatch+token quant of all {w.T} tokens "
+                       f"({t_route:.2f} s) + expert FFN of the {rows_done} rows routed to "
+                       f"{len(experts)} experts ({t_exp:.2f} s); algorithmic FLOPs of that "
+                       f"sample / wall time")}
+
+
+# ---------------------------------------------------------------------- main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_fp8", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(multi-GPU expert parallelism is not built)"}))
+        return 2
+
+    import fp8_grouped_gemm_amd as M
+    w = synth.WORKLOADS[a.workload]
+    if w.mode == "fp8" and a.workload == "prefill_fp8":
+        w = synth.scaled(w, m_align=16)
+    dev = torch.device("cuda:0")
+    log(f"workload {w}")
+    t0 = time.time()
+    inp, weights = make_layer(w, dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+    desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align)
+    ws = torch.empty(M.moe_layer_workspace_size(desc), dtype=torch.uint8, device=dev)
+    x = inp["x"]
+    ids = inp.get("token_ids")
+    y = torch.empty_like(x)
+    counts = torch.empty(w.E, dtype=torch.int32, device=dev)
+
+    def step():
+        M.moe_layer_fwd(desc, weights, x, ids, workspace=ws, y=y, counts=counts)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(a.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / a.steps
+    cnt = counts.cpu().numpy()
+    flops, bytes_, g = layer_flops_bytes(w, cnt)
+    log(f"layer {ms:.3f} ms/step; rows {g['rows']} touched experts {g['touched']}; "
+        f"loads max {cnt.max()} median {int(np.median(cnt))} min {cnt.min()}")
+
+    # per-stage times through the individual entry points (same kernels, same stream)
+    stages = {}
+    if not a.no_stages and w.mode == "fp8" and w.route == "score":
+        stages = stage_times(M, w, inp, weights, a.steps)
+        log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+    g1_ms = stages.get("gemm1")
+    roofline = None
+    if g1_ms:
+        achieved = g["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9
+        roofline = {"kernel": "grouped_gemm_fp8 (GEMM1: gate+up, SwiGLU, e4m3 requant)",
+                    "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": None, "avg_ms": round(g1_ms, 4),
+                    "tflops": round(g["gemm1_flops"] / (g1_ms * 1e-3) / 1e12, 1),
+                    "bytes_per_launch": g["gemm1_bytes"]}
+    out = {
+        "metric": "MoE layer FP8 grouped-GEMM TFLOPS + tokens/s on 1 MI355X (% roofline)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "layer_hbm_frac": round(bytes_ / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"fp8": "e4m3", "w4a16": "int4xbf16", "fp32": "f32"}[w.mode],
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: T={w.T} d={w.d} E={w.E} top-{w.k} I={w.I}",
+                   "mode": w.mode, "route": w.route, "m_align": w.m_align,
+                   "skew": f"+{w.skew_add} on {w.skew_frac:.0%} of experts" if w.skew_frac else None},
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()} or None,
+        "roofline": roofline,
+    }
+    if not a.no_cpu_baseline and w.mode == "fp8" and w.route == "score":
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def stage_times(M, w, inp, weights, steps):
+    """Average time of each step of the layer, run through the individual C entry points
+    on torch's current stream and bracketed by HIP events."""
+    dev = inp["x"].device
+    x = inp["x"]
+    names = ["route", "dispatch", "quant", "gemm1", "gemm2", "combine"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = {n: 0.0 for n in names}
+    R = M.moe_rows_bound(w.T, w.k, w.E, w.m_align)
+    for it in range(steps + 1):
+        ev[0].record()
+        idx, gw, _ = M.moe_route(x, inp["w_router"], inp["bias"], w.k)
+        ev[1].record()
+        counts, offsets, ros, sor = M.moe_dispatch(idx, w.E, w.m_align)
+        ev[2].record()
+        qx, sx = M.moe_quant_fp8(x)
+        ev[3].record()
+        hq, sh = M.grouped_gemm_fp8(qx, sx, weights["w13"], weights["s13"], offsets, R, w.I,
+                                    swiglu=True, a_rows=sor, a_row_div=w.k)
+        ev[4].record()
+        o = M.grouped_gemm_fp8(hq, sh, weights["w2"], weights["s2"], offsets, R, w.d)
+        ev[5].record()
+        M.moe_combine(o, ros, gw, w.T, w.k)
+        ev[6].record()
+        torch.cuda.synchronize()
+        if it == 0:
+            continue        # first pass warms the allocator
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    return {n: acc[n] / steps for n in names}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,257 @@
+"""MI355X (gfx950) forward pass of one Mixture-of-Experts FFN layer.
+
+A thin binding over the C ABI of ``libmoe_gfx950.so`` (include/moe.h): each function
+here has the C entry point's name, takes torch tensors that live on the GPU, allocates
+the outputs with torch and passes raw pointers plus the current HIP stream.  Every
+step runs in the library's HIP kernels; nothing is computed in Python.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_BF16, MOE_E4M3, MOE_EPI_PLAIN, MOE_EPI_SWIGLU, MOE_F32, MOE_INT4,
+                   MOE_MODE_FP32, MOE_MODE_FP8, MOE_MODE_W4A16, MOE_ROUTE_HASH,
+                   MOE_ROUTE_RENORM, MOE_ROUTE_SCORE, MoeError, MoeLayerDesc, MoeLayerWeights)
+
+__all__ = [
+    "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route",
+    "moe_route_from_logits", "moe_route_hash", "moe_dispatch", "moe_quant_fp8",
+    "moe_quant_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_w4a16",
+    "grouped_gemm_f32", "moe_combine", "moe_layer_workspace_size", "moe_layer_fwd", "MoeError",
+    "LayerDesc",
+]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _lib_():
+    return _lib.load()
+
+
+# --------------------------------------------------------------- host helpers
+
+def moe_device_supported(device: int = 0) -> bool:
+    return _lib_().moe_device_supported(device) == _lib.MOE_OK
+
+
+def moe_capacity(T: int, k: int, E: int, factor: float) -> int:
+    r = _lib_().moe_capacity(T, k, E, float(factor))
+    _lib.check(min(r, 0), "moe_capacity")
+    return r
+
+
+def moe_rows_bound(T: int, k: int, E: int, m_align: int) -> int:
+    return _lib_().moe_rows_bound(T, k, E, m_align)
+
+
+# -------------------------------------------------------------------- routing
+
+def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor, k: int,
+              renorm: bool = False):
+    """Router logits + biased softmax top-k.  Returns (topk_idx, topk_w, logits)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _lib.check(_lib_().moe_route(_ptr(x), _dt(x), _ptr(w_router), _ptr(bias), T, d, E, k,
+                                 MOE_ROUTE_RENORM if renorm else 0, _ptr(logits), _ptr(idx),
+                                 _ptr(w), _stream(dev)), "moe_route")
+    return idx, w, logits
+
+
+def moe_route_from_logits(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                          renorm: bool = False):
+    T, E = logits.shape
+    dev = logits.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _lib.check(_lib_().moe_route_from_logits(_ptr(logits), _ptr(bias), T, E, k,
+                                             MOE_ROUTE_RENORM if renorm else 0, _ptr(idx),
+                                             _ptr(w), _stream(dev)), "moe_route_from_logits")
+    return idx, w
+
+
+def moe_route_hash(token_ids: torch.Tensor, E: int):
+    T = token_ids.shape[0]
+    dev = token_ids.device
+    idx = torch.empty((T, 1), dtype=torch.int32, device=dev)
+    w = torch.empty((T, 1), dtype=torch.float32, device=dev)
+    _lib.check(_lib_().moe_route_hash(_ptr(token_ids), T, E, _ptr(idx), _ptr(w), _stream(dev)),
+               "moe_route_hash")
+    return idx, w
+
+
+def moe_dispatch(topk_idx: torch.Tensor, E: int, m_align: int, capacity: int = 0):
+    """Returns (counts [E], offsets [E+1], row_of_slot [T*k], slot_of_row [rows_bound])."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    R = moe_rows_bound(T, k, E, m_align)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ros = torch.empty(T * k, dtype=torch.int32, device=dev)
+    sor = torch.empty(R, dtype=torch.int32, device=dev)
+    _lib.check(_lib_().moe_dispatch(_ptr(topk_idx), T, k, E, m_align, capacity, _ptr(counts),
+                                    _ptr(offsets), _ptr(ros), _ptr(sor), _stream(dev)),
+               "moe_dispatch")
+    return counts, offsets, ros, sor
+
+
+# --------------------------------------------------------------- quantisation
+
+def moe_quant_fp8(x: torch.Tensor, src_row: Optional[torch.Tensor] = None, src_div: int = 1,
+                  rows_out: Optional[int] = None):
+    """1x128 e4m3 quantisation; returns (codes uint8 [rows_out, K], scales fp32)."""
+    rows_in, K = x.shape
+    rows_out = rows_in if rows_out is None else rows_out
+    dev = x.device
+    q = torch.empty((rows_out, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((rows_out, K // 128), dtype=torch.float32, device=dev)
+    _lib.check(_lib_().moe_quant_fp8(_ptr(x), _dt(x), rows_in, K, _ptr(src_row), src_div,
+                                     rows_out, _ptr(q), _ptr(s), _stream(dev)), "moe_quant_fp8")
+    return q, s
+
+
+def moe_quant_weight_fp8(w: torch.Tensor):
+    G, N, K = w.shape
+    dev = w.device
+    q = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=dev)
+    _lib.check(_lib_().moe_quant_weight_fp8(_ptr(w), G, N, K, _ptr(q), _ptr(s), _stream(dev)),
+               "moe_quant_weight_fp8")
+    return q, s
+
+
+def moe_quant_weight_int4(w: torch.Tensor):
+    G, N, K = w.shape
+    dev = w.device
+    q = torch.empty((G, N, K // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((G, N, K // 128), dtype=torch.float32, device=dev)
+    _lib.check(_lib_().moe_quant_weight_int4(_ptr(w), G, N, K, _ptr(q), _ptr(s), _stream(dev)),
+               "moe_quant_weight_int4")
+    return q, s
+
+
+# --------------------------------------------------------------- grouped GEMM
+
+def grouped_gemm_fp8(A, sA, B, sB, offsets, R_cap: int, N: int, swiglu: bool = False,
+                     a_rows: Optional[torch.Tensor] = None, a_row_div: int = 1):
+    """Returns C bf16 [R_cap, N] (plain) or (codes e4m3 [R_cap, N], sC [R_cap, N/128])."""
+    K = A.shape[1]
+    G = B.shape[0]
+    dev = A.device
+    if swiglu:
+        Cc = torch.empty((R_cap, N), dtype=torch.uint8, device=dev)
+        sC = torch.empty((R_cap, N // 128), dtype=torch.float32, device=dev)
+        out_dt, epi = MOE_E4M3, MOE_EPI_SWIGLU
+    else:
+        Cc = torch.empty((R_cap, N), dtype=torch.bfloat16, device=dev)
+        sC = None
+        out_dt, epi = MOE_BF16, MOE_EPI_PLAIN
+    _lib.check(_lib_().grouped_gemm_fp8(_ptr(A), _ptr(sA), _ptr(a_rows), a_row_div, _ptr(B),
+                                        _ptr(sB), _ptr(offsets), G, R_cap, N, K, epi, out_dt,
+                                        _ptr(Cc), _ptr(sC), _stream(dev)), "grouped_gemm_fp8")
+    return (Cc, sC) if swiglu else Cc
+
+
+def grouped_gemm_w4a16(A, B, s7, offsets, R_cap: int, N: int, swiglu: bool = False,
+                       a_rows: Optional[torch.Tensor] = None, a_row_div: int = 1):
+    K = A.shape[1]
+    G = B.shape[0]
+    dev = A.device
+    Cc = torch.empty((R_cap, N), dtype=torch.bfloat16, device=dev)
+    _lib.check(_lib_().grouped_gemm_w4a16(_ptr(A), _ptr(a_rows), a_row_div, _ptr(B), _ptr(s7),
+                                          _ptr(offsets), G, R_cap, N, K,
+                                          MOE_EPI_SWIGLU if swiglu else MOE_EPI_PLAIN, _ptr(Cc),
+                                          _stream(dev)), "grouped_gemm_w4a16")
+    return Cc
+
+
+def grouped_gemm_f32(A, B, offsets, R_cap: int, N: int, swiglu: bool = False,
+                     a_rows: Optional[torch.Tensor] = None, a_row_div: int = 1):
+    K = A.shape[1]
+    G = B.shape[0]
+    dev = A.device
+    Cc = torch.empty((R_cap, N), dtype=torch.float32, device=dev)
+    _lib.check(_lib_().grouped_gemm_f32(_ptr(A), _ptr(a_rows), a_row_div, _ptr(B), _ptr(offsets),
+                                        G, R_cap, N, K,
+                                        MOE_EPI_SWIGLU if swiglu else MOE_EPI_PLAIN, _ptr(Cc),
+                                        _stream(dev)), "grouped_gemm_f32")
+    return Cc
+
+
+def moe_combine(o: torch.Tensor, row_of_slot: torch.Tensor, topk_w: torch.Tensor, T: int, k: int,
+                out_dtype=torch.bfloat16):
+    d = o.shape[1]
+    dev = o.device
+    y = torch.empty((T, d), dtype=out_dtype, device=dev)
+    _lib.check(_lib_().moe_combine(_ptr(o), _dt(o), _ptr(row_of_slot), _ptr(topk_w), T, k, d,
+                                   _ptr(y), _dt(y), _stream(dev)), "moe_combine")
+    return y
+
+
+# ---------------------------------------------------------------------- layer
+
+class LayerDesc:
+    """Python view of moe_layer_desc."""
+
+    def __init__(self, T, d, E, k, I, mode="fp8", route="score", renorm=False,
+                 capacity_factor=0.0, m_align=128):
+        modes = {"fp32": MOE_MODE_FP32, "fp8": MOE_MODE_FP8, "w4a16": MOE_MODE_W4A16}
+        self.c = MoeLayerDesc(T, d, E, k, I, modes[mode],
+                              MOE_ROUTE_HASH if route == "hash" else MOE_ROUTE_SCORE,
+                              MOE_ROUTE_RENORM if renorm else 0, float(capacity_factor), m_align)
+
+
+def moe_layer_workspace_size(desc: LayerDesc) -> int:
+    n = _lib_().moe_layer_workspace_size(C.byref(desc.c))
+    if n == 0:
+        raise MoeError(_lib.MOE_ERR_INVALID_ARG, "moe_layer_workspace_size",
+                       _lib_().moe_last_error().decode())
+    return n
+
+
+def moe_layer_fwd(desc: LayerDesc, weights: dict, x: torch.Tensor,
+                  token_ids: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  y: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None):
+    """Whole layer forward.  ``weights`` holds w_router, bias, w13, s13, w2, s2 tensors
+    (as moe_layer_weights).  Returns (y, counts)."""
+    dev = x.device
+    ws_bytes = moe_layer_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty(x.shape, dtype=x.dtype, device=dev)
+    if counts is None:
+        counts = torch.empty(desc.c.E, dtype=torch.int32, device=dev)
+    w = MoeLayerWeights(*(_ptr(weights.get(n)) for n in ("w_router", "bias", "w13", "s13", "w2",
+                                                        "s2")))
+    _lib.check(_lib_().moe_layer_fwd(C.byref(desc.c), C.byref(w), _ptr(x), _ptr(token_ids),
+                                     _ptr(y), _ptr(workspace), workspace.numel(), _ptr(counts),
+                                     _stream(dev)), "moe_layer_fwd")
+    return y, counts

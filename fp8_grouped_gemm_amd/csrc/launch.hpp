@@ -1,0 +1,41 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).  Each one
+// enqueues its kernels on `s` and returns hipGetLastError(); arguments were checked
+// by the C ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_router(const void* x, bool bf16, const void* w, float* logits, int T, int d,
+                         int E, hipStream_t s);
+hipError_t launch_topk(const float* logits, const float* bias, int T, int E, int k, bool renorm,
+                       int32_t* idx, float* w, hipStream_t s);
+hipError_t launch_hash_route(const int64_t* ids, int T, int E, int32_t* idx, float* w,
+                             hipStream_t s);
+hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int m_align, int cap,
+                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                           int32_t* slot_of_row, int rows_bound, hipStream_t s);
+hipError_t launch_quant_act(const void* x, bool bf16, int K, const int32_t* src_row, int src_div,
+                            int rows_out, uint8_t* q, float* scales, hipStream_t s);
+hipError_t launch_quant_weight_fp8(const float* w, int G, int N, int K, uint8_t* q,
+                                   float* scales, hipStream_t s);
+hipError_t launch_quant_weight_int4(const float* w, int G, int N, int K, uint8_t* q, float* s7,
+                                    hipStream_t s);
+// bm: rows per tile (16, 32, 64, 128; 128 only without SwiGLU)
+hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows,
+                           int a_row_div, const uint8_t* B, const float* sB,
+                           const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
+                           void* C, float* sC, int bm, int num_cus, hipStream_t s);
+hipError_t launch_gemm_w4a16(const uint16_t* A, const int32_t* a_rows, int a_row_div,
+                             const uint8_t* B, const float* s7, const int32_t* offsets, int G,
+                             int R_cap, int N, int K, bool swiglu, uint16_t* C, int num_cus,
+                             hipStream_t s);
+hipError_t launch_gemm_f32(const float* A, const int32_t* a_rows, int a_row_div, const float* B,
+                           const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
+                           float* C, hipStream_t s);
+hipError_t launch_combine(const void* o, bool o_bf16, const int32_t* row_of_slot,
+                          const float* w, int T, int k, int d, void* y, bool y_bf16,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,227 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE FFN layer forward library.
+ *
+ * The library computes the forward pass of one Mixture-of-Experts FFN layer on
+ * one GPU's batch of tokens:
+ *   route (biased fp32 softmax top-k, or hash)  ->  dispatch into expert-contiguous
+ *   rows  ->  1x128 e4m3 activation quantisation  ->  grouped FP8 GEMM with 128x128
+ *   block-scaled weights, fused SwiGLU and requantisation  ->  grouped FP8 down
+ *   projection  ->  weighted combine,
+ * as the MegaMoE/DeepGEMM walkthrough (discosf.com) describes it in sec. 2.1-2.2
+ * (layer maths) and sec. 3.2-3.3 (grouped GEMM and FP8), with the hash routing
+ * and 4-bit block weights of the DeepSeek-V4 lecture (tqpw.cn, sec. 2.2 and 3.1).
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a DEVICE pointer owned by the caller (host-side scalars are
+ *     passed by value).  The library allocates no device memory, keeps no pointer
+ *     after it returns and never synchronises the host: each call only enqueues
+ *     kernels on `stream` (a hipStream_t passed as void*; NULL = the null stream).
+ *   - Row-major layouts.  GEMM operands are K-contiguous ("NT"): A is [rows, K],
+ *     B is [G, N, K]; K, and the hidden and intermediate sizes, are multiples of 128.
+ *   - Arguments are checked before anything is launched; a bad argument returns a
+ *     negative moe_status and leaves every buffer untouched.  A device that is not
+ *     gfx950 gives MOE_ERR_UNSUPPORTED (the analogue of the walkthrough's "FP8 not
+ *     supported on this GPU", sec. 5.1).  A failed launch gives MOE_ERR_HIP.  Device
+ *     faults surface at the caller's next synchronisation.  moe_last_error() holds a
+ *     thread-local message for the last non-OK status.
+ *   - Outputs are fully overwritten (no accumulate mode).  Identical inputs give
+ *     bitwise identical outputs: no floating-point atomics are used.
+ *   - Calls on different streams may run concurrently; calls on one stream are
+ *     ordered by the stream.
+ */
+#ifndef FP8GG_MOE_H
+#define FP8GG_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* bad shape, dtype, flag or null pointer */
+  MOE_ERR_UNSUPPORTED = -2,  /* current device is not gfx950 / no device */
+  MOE_ERR_HIP = -3,          /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_WORKSPACE = -4     /* workspace smaller than moe_layer_workspace_size() */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,   /* IEEE fp32 */
+  MOE_BF16 = 1,  /* bfloat16 stored as uint16 */
+  MOE_E4M3 = 2,  /* OCP e4m3 ("fn": max 448, no infinities) stored as uint8 */
+  MOE_INT4 = 3   /* signed 4-bit codes in [-7, 7], two per byte, low nibble first */
+} moe_dtype;
+
+/* moe_route flags */
+#define MOE_ROUTE_RENORM 1u  /* divide the k gate weights by their sum */
+
+/* grouped GEMM epilogues */
+#define MOE_EPI_PLAIN 0       /* C = A.B^T written in the output dtype of the call   */
+#define MOE_EPI_SWIGLU 1      /* B holds 2N rows: [0,N) gate, [N,2N) up;              */
+                              /* C = silu(A.Bg^T) * (A.Bu^T), N columns              */
+
+/* layer modes */
+#define MOE_MODE_FP32 0   /* fp32 activations and weights, no quantisation            */
+#define MOE_MODE_FP8 1    /* e4m3 weights with 128x128 scales, 1x128 activation quant */
+#define MOE_MODE_W4A16 2  /* int4 weights with 1x128 per-channel scales, bf16 acts    */
+#define MOE_ROUTE_SCORE 0 /* biased softmax top-k over router logits                  */
+#define MOE_ROUTE_HASH 1  /* expert = ((id * 2654435761) mod 2^32) mod E, weight 1, k=1 */
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* MOE_OK when HIP device `hip_device` is a gfx950 (MI355X-class) GPU. */
+int moe_device_supported(int hip_device);
+
+/* Expert capacity floor(ceil(T*k/E) * factor); 0 when factor <= 0 (dropless).
+ * Reproduces ceil(T*k/E)*2 (DeepSeek MoE architecture, mooersco.com, ch. 1) and the
+ * worked value 76 for T=2048, k=2, E=64, factor 1.2 (same page, sec. 2.5).
+ * Host-only, pure.  Returns a negative moe_status on bad arguments. */
+int moe_capacity(int T, int k, int E, double factor);
+
+/* Rows an expert-contiguous buffer may need: T*k + E*(m_align-1).  Host-only. */
+size_t moe_rows_bound(int T, int k, int E, int m_align);
+
+/* Router: logits = x . w_router^T, then the biased softmax top-k of
+ * moe_route_from_logits.  s_i = softmax(W_g x + b_i) (discosf.com sec. 2.2); the
+ * softmax runs in fp32 (tqpw.cn sec. 2.3).
+ *   x [T, d] and w_router [E, d] of dtype x_dt (MOE_BF16 or MOE_F32, both the same);
+ *   bias [E] fp32; logits [T, E] fp32 output (required: it is the staging buffer);
+ *   topk_idx [T, k] int32 and topk_w [T, k] fp32 outputs.
+ *   1 <= k <= E <= 1024; d a multiple of 128 for MOE_BF16. */
+int moe_route(const void *x, moe_dtype x_dt, const void *w_router, const float *bias,
+              int T, int d, int E, int k, unsigned flags, float *logits,
+              int32_t *topk_idx, float *topk_w, void *stream);
+
+/* Top-k of fp32 logits [T, E] with per-expert bias [E] (bias may be NULL = 0).
+ * key_e = fl32(logit_e + b_e); the k largest keys are chosen, largest first, equal
+ * keys to the lower expert index; topk_w[t, j] = softmax over all E keys at
+ * topk_idx[t, j] (or, with MOE_ROUTE_RENORM, divided by the sum of the k chosen).
+ * Logits must be finite.  1 <= k <= E <= 1024. */
+int moe_route_from_logits(const float *logits, const float *bias, int T, int E, int k,
+                          unsigned flags, int32_t *topk_idx, float *topk_w, void *stream);
+
+/* Hash routing (tqpw.cn sec. 2.2): topk_idx[t] = ((id_t * 2654435761) mod 2^32) mod E,
+ * topk_w[t] = 1; k = 1.  token_ids [T] int64 (non-negative); E >= 1. */
+int moe_route_hash(const int64_t *token_ids, int T, int E, int32_t *topk_idx,
+                   float *topk_w, void *stream);
+
+/* Dispatch of routed slots into expert-contiguous rows (expert grouping,
+ * discosf.com sec. 2.1; capacity drop, mooersco.com sec. 2.5).  Slot s = t*k + j.
+ *   counts [E]        slots routed to each expert (before capacity)
+ *   offsets [E+1]     offsets[0] = 0, offsets[e+1] = offsets[e] + roundup(kept_e, m_align),
+ *                     kept_e = min(counts[e], capacity) (counts[e] when capacity = 0)
+ *   row_of_slot [T*k] row of each slot, -1 if dropped; within an expert rows follow
+ *                     slot order (stable)
+ *   slot_of_row [moe_rows_bound(T,k,E,m_align)]  inverse map, -1 on padding rows and
+ *                     on every row >= offsets[E]
+ * topk_idx [T, k] int32 in [0, E).  1 <= m_align <= 1024; capacity >= 0 (0 = dropless).
+ * Integer-only and deterministic. */
+int moe_dispatch(const int32_t *topk_idx, int T, int k, int E, int m_align, int capacity,
+                 int32_t *counts, int32_t *offsets, int32_t *row_of_slot,
+                 int32_t *slot_of_row, void *stream);
+
+/* 1x128 e4m3 activation quantisation (discosf.com sec. 3.3; fine-grained scales,
+ * qidao123.com day 3).  For output row r, source row i = src_row ? src_row[r] / src_div
+ * : r (src_row[r] < 0 gives an all-zero row with scale 1); for each 128-wide block:
+ * s = fl32(amax / 448) (1 if amax = 0), q = e4m3_rne(clamp(fl32(x / s), -448, 448)).
+ *   x [rows_in, K] of dtype x_dt (MOE_BF16 or MOE_F32); q [rows_out, K] uint8;
+ *   scales [rows_out, K/128] fp32.  K a multiple of 128; src_div >= 1. */
+int moe_quant_fp8(const void *x, moe_dtype x_dt, int rows_in, int K, const int32_t *src_row,
+                  int src_div, int rows_out, uint8_t *q, float *scales, void *stream);
+
+/* 128x128 block e4m3 weight quantisation with the same rule, one scale per block:
+ * w [G, N, K] fp32 -> q [G, N, K] uint8, scales [G, N/128, K/128] fp32.
+ * N and K multiples of 128. */
+int moe_quant_weight_fp8(const float *w, int G, int N, int K, uint8_t *q, float *scales,
+                         void *stream);
+
+/* Block-wise int4 weights with 1x128 per-channel blocks (tqpw.cn sec. 3.1): for each
+ * row n and 128-wide block, scale = max|w| (1 if 0), q = rne(fl32(fl32(w/scale)*7))
+ * in [-7,7], s7 = fl32(scale/7).  w [G, N, K] fp32 -> q [G, N, K/2] packed (element
+ * 2j in the low nibble), s7 [G, N, K/128] fp32.  K a multiple of 128. */
+int moe_quant_weight_int4(const float *w, int G, int N, int K, uint8_t *q, float *s7,
+                          void *stream);
+
+/* Grouped FP8 GEMM (discosf.com sec. 3.2: groups differ in M, share N and K; two-level
+ * accumulation with fine-grained scales, qidao123.com day 3).  Group g owns logical
+ * rows [offsets[g], offsets[g+1]) (offsets on the device, non-decreasing, offsets[0]=0,
+ * offsets[G] <= R_cap).  Logical row r reads A row a = a_rows ? a_rows[r] / a_row_div
+ * : r (a_rows[r] < 0: any row, output unspecified).  For each 128-deep K block kb
+ * the e4m3 products are summed in fp32 and promoted as
+ *   acc += sA[a, kb] * sB[g, n/128, kb] * partial.
+ *   A [*, K] e4m3, sA [*, K/128] fp32; B [G, Nb, K] e4m3, sB [G, Nb/128, K/128] fp32
+ *   with Nb = N (MOE_EPI_PLAIN) or 2N (MOE_EPI_SWIGLU).
+ *   out_dt MOE_BF16: C [R_cap, N] bf16 (RNE), sC unused;
+ *   out_dt MOE_E4M3 (SwiGLU only): C [R_cap, N] e4m3 codes of the fp32 SwiGLU output
+ *     quantised 1x128 as moe_quant_fp8, sC [R_cap, N/128] fp32.
+ * Rows >= offsets[G] and padding rows are unspecified.  N and K multiples of 128. */
+int grouped_gemm_fp8(const uint8_t *A, const float *sA, const int32_t *a_rows, int a_row_div,
+                     const uint8_t *B, const float *sB, const int32_t *offsets, int G,
+                     int R_cap, int N, int K, int epilogue, moe_dtype out_dt, void *C,
+                     float *sC, void *stream);
+
+/* Grouped GEMM with int4 weights and bf16 activations: B codes [G, Nb, K/2] and
+ * s7 [G, Nb, K/128] are dequantised in-kernel to bf16(fl32(q * s7)) and multiplied with
+ * A [*, K] bf16 in fp32.  Row gather and epilogues as grouped_gemm_fp8; output C
+ * [R_cap, N] bf16.  N multiple of 64, K multiple of 128. */
+int grouped_gemm_w4a16(const uint16_t *A, const int32_t *a_rows, int a_row_div,
+                       const uint8_t *B, const float *s7, const int32_t *offsets, int G,
+                       int R_cap, int N, int K, int epilogue, uint16_t *C, void *stream);
+
+/* Grouped fp32 GEMM (no quantisation): A [*, K] fp32, B [G, Nb, K] fp32, C [R_cap, N]
+ * fp32.  Row gather and epilogues as grouped_gemm_fp8.  N multiple of 16, K >= 1. */
+int grouped_gemm_f32(const float *A, const int32_t *a_rows, int a_row_div, const float *B,
+                     const int32_t *offsets, int G, int R_cap, int N, int K, int epilogue,
+                     float *C, void *stream);
+
+/* Weighted combine (y = sum over the top-k of G(x)_i E_i(x), discosf.com sec. 2.1):
+ * y[t] = sum_j topk_w[t,j] * o[row_of_slot[t*k+j]] in fp32, j = 0..k-1 in order,
+ * slots with row -1 skipped; o [*, d] and y [T, d] of dtype MOE_BF16 or MOE_F32.
+ * d a multiple of 8.  A deterministic gather: no atomics. */
+int moe_combine(const void *o, moe_dtype o_dt, const int32_t *row_of_slot,
+                const float *topk_w, int T, int k, int d, void *y, moe_dtype y_dt,
+                void *stream);
+
+typedef struct {
+  int T, d, E, k, I;       /* tokens, hidden, experts, top-k, expert intermediate size */
+  int mode;                /* MOE_MODE_*                                            */
+  int route;               /* MOE_ROUTE_SCORE or MOE_ROUTE_HASH (k must be 1)       */
+  unsigned route_flags;    /* MOE_ROUTE_RENORM                                      */
+  double capacity_factor;  /* <= 0: dropless                                        */
+  int m_align;             /* row padding quantum of each expert (1..1024)          */
+} moe_layer_desc;
+
+typedef struct {
+  const void *w_router;    /* [E, d]: bf16 (FP8/W4A16 modes) or fp32 (FP32 mode)    */
+  const float *bias;       /* [E] fp32 (score routing)                              */
+  const void *w13;         /* [E, 2I, d]: rows [0,I) gate, [I,2I) up.  fp32 | e4m3 | */
+                           /*   int4 packed [E, 2I, d/2]                             */
+  const float *s13;        /* FP8: [E, 2I/128, d/128]; W4A16: [E, 2I, d/128]        */
+  const void *w2;          /* [E, d, I] (int4: [E, d, I/2])                         */
+  const float *s2;         /* FP8: [E, d/128, I/128]; W4A16: [E, d, I/128]          */
+} moe_layer_weights;
+
+/* Bytes of device workspace moe_layer_fwd needs for `desc` (0 on a bad descriptor). */
+size_t moe_layer_workspace_size(const moe_layer_desc *desc);
+
+/* The whole layer forward on one stream, no host synchronisation:
+ * route -> dispatch -> (FP8: per-token 1x128 quant) -> grouped GEMM1 with SwiGLU
+ * (FP8: requantised 1x128) -> grouped GEMM2 -> combine.
+ *   x [T, d]: fp32 (FP32 mode) or bf16; token_ids [T] int64 for hash routing;
+ *   y [T, d] output: fp32 (FP32 mode) or bf16;
+ *   ws / ws_bytes: caller-owned device workspace (>= moe_layer_workspace_size);
+ *   counts_out [E] int32 (may be NULL): routed slots per expert.
+ * GEMM1 reads activation rows through the dispatch map, so no gathered copy of the
+ * activations is made. */
+int moe_layer_fwd(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                  const int64_t *token_ids, void *y, void *ws, size_t ws_bytes,
+                  int32_t *counts_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8GG_MOE_H */

@@ -199,7 +199,7 @@ def combine(o, row_of_slot, w, T: int, k: int) -> np.ndarray:
 
 def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
                   w_router=None, bias=None, token_ids=None, renorm: bool = False,
-                  cap_factor: float = 0.0, experts=None, tokens=None):
+                  cap_factor: float = 0.0, experts=None, tokens=None, keep: bool = False):
     """One MoE FFN layer forward on one GPU's batch, fp64.
 
     mode "fp32":  w13 [E,2I,d], w2 [E,d,I] fp32 arrays in ``experts``; no quantisation.
@@ -212,7 +212,9 @@ def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
     Routing: score (softmax + bias top-k) when ``w_router`` is given, else hash.
     ``tokens`` (optional) restricts the expert computation to those tokens (every
     routing decision is still made for the whole batch); y rows of other tokens
-    are NaN.
+    are NaN.  ``keep`` also returns, per computed slot, the activation row, the exact
+    g, u and h = swiglu(g, u) before requantisation, and the dequantised weights of
+    every expert used (for error analysis in tests).
     Returns a dict with logits32, idx, w, dispatch outputs, o rows and y (fp64).
     """
     x = np.asarray(x)
@@ -239,7 +241,7 @@ def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
     else:
         xin = xf.astype(np.float64)
 
-    o = {}
+    o, info, deq = {}, {}, {}
     for e in range(E):
         rows = np.arange(offsets[e], offsets[e + 1])
         slots = sor[rows]
@@ -262,6 +264,7 @@ def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
             w2 = int4_dequant(c2[e:e + 1], s2[e:e + 1])[0].astype(np.float64)
         gu = a @ w13.T
         h = swiglu(gu[:, :I], gu[:, I:])
+        h_exact = h
         if mode == "fp8":
             qh, sh = quant_fp8_act(h.astype(np.float32))
             h = dequant_fp8_act(qh, sh)
@@ -270,6 +273,11 @@ def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
         oe = h @ w2.T
         for i, s in enumerate(slots):
             o[int(s)] = oe[i]
+            if keep:
+                info[int(s)] = {"e": e, "a": a[i], "g": gu[i, :I], "u": gu[i, I:],
+                                "h": h_exact[i], "h_used": h[i]}
+        if keep:
+            deq[e] = (w13, w2)
     y = np.full((T, d), np.nan, dtype=np.float64)
     wk = np.asarray(w).reshape(T, k)
     for t in np.nonzero(want)[0]:
@@ -281,4 +289,6 @@ def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
         y[t] = acc
     out["o_by_slot"] = o
     out["y"] = y
+    if keep:
+        out["slot_info"], out["experts_deq"] = info, deq
     return out

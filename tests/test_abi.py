@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching a device.  No kernel runs here."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from fp8_grouped_gemm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = C.c_void_p(0x1000)   # never dereferenced: validation rejects the call first
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*"
+                       r"([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_symbols_exported():
+    lib = _lib.load()
+    declared = _declared()
+    assert len(declared) == 17, declared
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+    assert sorted(_lib.SIGNATURES) == declared
+
+
+def test_capacity_and_rows_bound(golden):
+    lib = _lib.load()
+    ex = golden["capacity_example"]
+    assert lib.moe_capacity(ex["T"], ex["k"], ex["E"], ex["factor"]) == ex["value"]
+    assert lib.moe_capacity(4096, 8, 256, 2.0) == 256
+    assert lib.moe_capacity(100, 2, 7, 2.0) == 58   # ceil(200/7) = 29 -> 58
+    assert lib.moe_capacity(10, 2, 4, 0.0) == 0
+    assert lib.moe_capacity(-1, 2, 4, 1.0) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_rows_bound(4096, 8, 256, 128) == 4096 * 8 + 256 * 127
+    assert lib.moe_rows_bound(4096, 8, 256, 0) == 0
+
+
+def _err(status, fragment=None):
+    lib = _lib.load()
+    assert status == _lib.MOE_ERR_INVALID_ARG
+    msg = lib.moe_last_error().decode()
+    assert msg
+    if fragment:
+        assert fragment in msg, msg
+
+
+def test_route_rejects_bad_args():
+    lib = _lib.load()
+    S = None
+    _err(lib.moe_route_from_logits(None, None, 4, 8, 2, 0, FAKE, FAKE, S), "null")
+    _err(lib.moe_route_from_logits(FAKE, None, 4, 8, 9, 0, FAKE, FAKE, S), "k must")
+    _err(lib.moe_route_from_logits(FAKE, None, 4, 2000, 2, 0, FAKE, FAKE, S), "E must")
+    _err(lib.moe_route_from_logits(FAKE, None, 4, 8, 2, 4, FAKE, FAKE, S), "flags")
+    _err(lib.moe_route(FAKE, _lib.MOE_E4M3, FAKE, FAKE, 4, 256, 8, 2, 0, FAKE, FAKE, FAKE, S),
+         "x_dt")
+    _err(lib.moe_route(FAKE, _lib.MOE_BF16, FAKE, FAKE, 4, 200, 8, 2, 0, FAKE, FAKE, FAKE, S),
+         "128")
+    _err(lib.moe_route_hash(None, 4, 8, FAKE, FAKE, S), "null")
+
+
+def test_dispatch_and_quant_reject_bad_args():
+    lib = _lib.load()
+    S = None
+    _err(lib.moe_dispatch(FAKE, 4, 2, 8, 0, 0, FAKE, FAKE, FAKE, FAKE, S), "m_align")
+    _err(lib.moe_dispatch(FAKE, 4, 2, 8, 16, -1, FAKE, FAKE, FAKE, FAKE, S), "capacity")
+    _err(lib.moe_dispatch(FAKE, 4, 2, 8, 16, 0, None, FAKE, FAKE, FAKE, S), "null")
+    _err(lib.moe_quant_fp8(FAKE, _lib.MOE_BF16, 4, 100, None, 1, 4, FAKE, FAKE, S), "K must")
+    _err(lib.moe_quant_fp8(FAKE, _lib.MOE_BF16, 4, 128, None, 1, 8, FAKE, FAKE, S), "rows_out")
+    _err(lib.moe_quant_fp8(FAKE, _lib.MOE_INT4, 4, 128, None, 1, 4, FAKE, FAKE, S), "x_dt")
+    _err(lib.moe_quant_weight_fp8(FAKE, 1, 100, 128, FAKE, FAKE, S), "multiples of 128")
+    _err(lib.moe_quant_weight_int4(FAKE, 1, 8, 100, FAKE, FAKE, S), "K must")
+
+
+def test_gemm_and_combine_reject_bad_args():
+    lib = _lib.load()
+    S = None
+    _err(lib.grouped_gemm_fp8(FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 0, 128, 128, 128, 0,
+                              _lib.MOE_BF16, FAKE, None, S), "G must")
+    _err(lib.grouped_gemm_fp8(FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 2, 128, 100, 128, 0,
+                              _lib.MOE_BF16, FAKE, None, S), "multiples of 128")
+    _err(lib.grouped_gemm_fp8(FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 2, 128, 128, 128, 1,
+                              _lib.MOE_BF16, FAKE, None, S), "SwiGLU")
+    _err(lib.grouped_gemm_fp8(FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 2, 128, 128, 128, 7,
+                              _lib.MOE_BF16, FAKE, None, S), "epilogue")
+    _err(lib.grouped_gemm_fp8(FAKE, None, None, 1, FAKE, FAKE, FAKE, 2, 128, 128, 128, 0,
+                              _lib.MOE_BF16, FAKE, None, S), "scale")
+    _err(lib.grouped_gemm_w4a16(FAKE, None, 1, FAKE, FAKE, FAKE, 2, 64, 96, 128, 1, FAKE, S),
+         "multiple of 64")
+    _err(lib.grouped_gemm_f32(FAKE, None, 1, FAKE, FAKE, 2, 64, 24, 128, 0, FAKE, S),
+         "multiple of 16")
+    _err(lib.moe_combine(FAKE, _lib.MOE_BF16, FAKE, FAKE, 4, 2, 12, FAKE, _lib.MOE_BF16, S),
+         "multiple of 8")
+    _err(lib.moe_combine(FAKE, _lib.MOE_E4M3, FAKE, FAKE, 4, 2, 16, FAKE, _lib.MOE_BF16, S),
+         "dtypes")
+
+
+def test_layer_descriptor_checks_and_workspace():
+    lib = _lib.load()
+    D = _lib.MoeLayerDesc
+    good = D(4096, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.0, 128)
+    n = lib.moe_layer_workspace_size(C.byref(good))
+    R = 4096 * 8 + 256 * 127
+    # the big pieces: token codes, h codes, bf16 expert outputs
+    assert n >= 4096 * 7168 + R * 2048 + R * 7168 * 2
+    assert n < (4096 * 7168 + R * 2048 + R * 7168 * 2) * 1.05
+    bad = D(4096, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_HASH, 0, 0.0, 128)
+    assert lib.moe_layer_workspace_size(C.byref(bad)) == 0       # hash needs k = 1
+    assert "hash" in lib.moe_last_error().decode()
+    bad = D(16, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.0, 0)
+    assert lib.moe_layer_workspace_size(C.byref(bad)) == 0
+    w = _lib.MoeLayerWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    st = lib.moe_layer_fwd(C.byref(good), C.byref(w), FAKE, None, FAKE, FAKE, 16, None, None)
+    assert st == _lib.MOE_ERR_WORKSPACE
+    w = _lib.MoeLayerWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE)
+    st = lib.moe_layer_fwd(C.byref(good), C.byref(w), FAKE, None, FAKE, FAKE, n, None, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

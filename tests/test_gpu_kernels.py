@@ -1,0 +1,326 @@
+"""GPU parity of every C-ABI step against the CPU oracle on the same seeded inputs.
+
+Integer results (codes, indices, counts, offsets, permutations) must be bit-exact;
+floating-point results are held to max|err beyond the prescribed output rounding| /
+max|ref| <= 2e-3 (the raw ratio is reported beside it).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_grouped_gemm_amd as M
+import oracle as O
+from oracle import codecs as OC
+import synth
+from gpu_util import (TOL, dev, error_ratios, note, requant_band, swiglu_error_model,
+                      to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+# -------------------------------------------------------------- quantisation
+
+def test_e4m3_conversion_every_boundary():
+    """Blocks whose largest element is 448 have scale 1, so the codes are the direct
+    conversion of the other 127 values: sweep every representable value, every
+    midpoint (ties) and its neighbours one fp32 ulp away."""
+    note("e4m3 conversion sweep")
+    t = OC.e4m3_decode_table()
+    pos = np.sort(np.unique(np.abs(t[np.isfinite(t)])))
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = np.concatenate([pos, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(1e9)),
+                           np.float32([1e-30, 2.0 ** -12, 3 * 2.0 ** -11, 447.9, 440.0])])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    n = len(vals)
+    nblk = (n + 126) // 127
+    x = np.zeros((nblk, 128), np.float32)
+    flat = np.zeros(nblk * 127, np.float32)
+    flat[:n] = vals
+    x[:, 1:] = flat.reshape(nblk, 127)
+    x[:, 0] = 448.0
+    q, s = M.moe_quant_fp8(torch.from_numpy(x).to(dev()))
+    qo, so = OC.quant_fp8_act(x)
+    np.testing.assert_array_equal(to_np(s), so)
+    assert np.all(so == 1.0)
+    np.testing.assert_array_equal(to_np(q), qo)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quant_act_bitexact(dtype):
+    note(f"quant act {dtype}")
+    x = synth.normal((37, 640), 5, "x", dtype=dtype)
+    x[3, 128:256] = 0                        # all-zero block -> scale 1, zero codes
+    x[4, :128] *= 1e-3
+    x[5, 256:384] *= 300.0
+    q, s = M.moe_quant_fp8(x.to(dev()))
+    qo, so = OC.quant_fp8_act(x.float().numpy())
+    np.testing.assert_array_equal(to_np(s), so)
+    np.testing.assert_array_equal(to_np(q), qo)
+
+
+def test_quant_act_gather():
+    note("quant act gather")
+    T, k, K = 21, 3, 256
+    x = synth.normal((T, K), 6, "x", dtype=torch.bfloat16)
+    src = np.array([5, -1, 62, 0, 11, -1, 30, 45], np.int32)   # slots; token = slot // k
+    q, s = M.moe_quant_fp8(x.to(dev()), torch.from_numpy(src).to(dev()), k, len(src))
+    qo, so = OC.quant_fp8_act(x.float().numpy())
+    for r, sl in enumerate(src):
+        if sl < 0:
+            assert np.all(to_np(q[r]) == 0) and np.all(to_np(s[r]) == 1.0)
+        else:
+            np.testing.assert_array_equal(to_np(q[r]), qo[sl // k])
+            np.testing.assert_array_equal(to_np(s[r]), so[sl // k])
+
+
+def test_quant_weight_fp8_bitexact():
+    note("quant weight fp8")
+    w = synth.normal((3, 256, 384), 7, "w13", std=0.02)
+    w[1, :128, :128] = 0
+    q, s = M.moe_quant_weight_fp8(w.to(dev()))
+    qo, so = OC.quant_fp8_weight(w.numpy())
+    np.testing.assert_array_equal(to_np(s), so)
+    np.testing.assert_array_equal(to_np(q), qo)
+
+
+def test_quant_weight_int4_bitexact():
+    note("quant weight int4")
+    w = synth.normal((2, 40, 384), 8, "w2", std=0.02)
+    w[0, 3, :128] = 0
+    q, s7 = M.moe_quant_weight_int4(w.to(dev()))
+    qo, so = OC.int4_quant_rows(w.numpy())
+    np.testing.assert_array_equal(to_np(s7), so)
+    np.testing.assert_array_equal(to_np(q), OC.int4_pack(qo))
+
+
+# -------------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("T,E,k,ties,renorm", [(300, 256, 8, False, False),
+                                               (300, 256, 8, True, False),
+                                               (77, 8, 2, True, True),
+                                               (50, 64, 6, False, True),
+                                               (40, 1000, 7, True, False),
+                                               (33, 5, 5, False, False)])
+def test_route_from_logits(T, E, k, ties, renorm):
+    note(f"topk T={T} E={E} k={k} ties={ties} renorm={renorm}")
+    L = synth.random_logits(T, E, seed=E + k, ties=ties)
+    b = synth.uniform((E,), -0.01, 0.01, 3, "bias")
+    if ties:
+        b = torch.round(b * 100) / 100 * 0   # keep exact ties in the keys
+    idx, w = M.moe_route_from_logits(L.to(dev()), b.to(dev()), k, renorm)
+    io, wo = O.topk_route(L.numpy(), b.numpy(), k, renorm)
+    np.testing.assert_array_equal(to_np(idx), io)
+    # fp32 softmax vs fp64: a few ulp per exp and per partial sum
+    np.testing.assert_allclose(to_np(w), wo, rtol=2e-5, atol=0)
+
+
+@pytest.mark.parametrize("dtype,T,d,E", [(torch.bfloat16, 200, 512, 256),
+                                         (torch.bfloat16, 70, 7168, 64),
+                                         (torch.float32, 256, 256, 8)])
+def test_router_logits(dtype, T, d, E):
+    note(f"router logits {dtype} T={T} d={d} E={E}")
+    x = synth.normal((T, d), 9, "x", dtype=dtype)
+    w = synth.normal((E, d), 9, "w_gate_router", std=d ** -0.5, dtype=dtype)
+    b = synth.uniform((E,), -0.01, 0.01, 9, "bias")
+    idx, gw, logits = M.moe_route(x.to(dev()), w.to(dev()), b.to(dev()), 2)
+    ref = O.router_logits(x.float().numpy(), w.float().numpy())
+    # fp32 accumulation of d exact products: |err| <= d * 2^-24 * sum|x_i w_i|
+    bound = d * 2.0 ** -24 * (np.abs(x.float().numpy()) @ np.abs(w.float().numpy()).T)
+    assert np.all(np.abs(to_np(logits) - ref) <= bound + 1e-30)
+    # the top-k of the GPU's own fp32 logits is bit-exact
+    io, _ = O.topk_route(to_np(logits), b.numpy(), 2)
+    np.testing.assert_array_equal(to_np(idx), io)
+
+
+def test_hash_route():
+    note("hash route")
+    ids = torch.randint(0, 129280, (5000,), generator=torch.Generator().manual_seed(1),
+                        dtype=torch.int64)
+    ids[:4] = torch.tensor([0, 1, 2, 2 ** 40 + 7])
+    idx, w = M.moe_route_hash(ids.to(dev()), 64)
+    io, wo = O.hash_route(ids.numpy(), 64)
+    np.testing.assert_array_equal(to_np(idx), io)
+    assert np.all(to_np(w) == 1.0)
+
+
+# ------------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("T,E,k,m_align,cap", [(4096, 256, 8, 128, 0), (128, 256, 8, 16, 0),
+                                               (500, 64, 1, 128, 0), (333, 13, 3, 32, 0),
+                                               (333, 13, 3, 16, 40), (1, 4, 2, 1, 0),
+                                               (0, 4, 2, 16, 0), (2048, 64, 2, 64, 76)])
+def test_dispatch_bitexact(T, E, k, m_align, cap):
+    note(f"dispatch T={T} E={E} k={k} m_align={m_align} cap={cap}")
+    idx = synth.random_topk(T, E, k, seed=T + E, skew=1.1) if T else np.zeros((0, k), np.int32)
+    counts, offsets, ros, sor = M.moe_dispatch(torch.from_numpy(idx).to(dev()), E, m_align, cap)
+    co, oo, ro, so = O.dispatch(idx, E, m_align, cap)
+    np.testing.assert_array_equal(to_np(counts), co)
+    np.testing.assert_array_equal(to_np(offsets), oo)
+    np.testing.assert_array_equal(to_np(ros), ro)
+    np.testing.assert_array_equal(to_np(sor), so)
+
+
+# ---------------------------------------------------------------- grouped GEMM
+
+def _gemm_case(sizes, N, K, m_align, seed, swiglu):
+    sizes = np.asarray(sizes)
+    G = len(sizes)
+    padded = -(-sizes // m_align) * m_align
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    R = int(offsets[-1]) + 7                      # a few rows past the last group
+    a = synth.normal((R, K), seed, "gemm_a")
+    for g in range(G):                            # padding rows hold zeros
+        a[offsets[g] + sizes[g]:offsets[g + 1]] = 0
+    Nb = 2 * N if swiglu else N
+    b = synth.normal((G, Nb, K), seed, "gemm_b", std=K ** -0.5)
+    return a, b, offsets, R
+
+
+@pytest.mark.parametrize("sizes,m_align", [
+    ([128, 256, 64, 512, 128, 256, 64, 512], 128),   # the page's group-size example
+    ([0, 1, 17, 130, 300, 0], 16),                     # empty, tiny, ragged groups
+    ([5, 3, 9, 2, 7, 1, 4, 6, 8, 3], 8),              # decode-sized groups (bm 16)
+    ([40, 33, 50, 20], 32),                            # bm 32
+    ([90, 70, 100], 64),                               # bm 64
+])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_fp8(sizes, m_align, swiglu):
+    N, K = 256, 512
+    note(f"gemm fp8 sizes={sizes} m_align={m_align} swiglu={swiglu}")
+    a, b, offsets, R = _gemm_case(sizes, N, K, m_align, 11, swiglu)
+    qa, sa = M.moe_quant_fp8(a.to(dev()))
+    qb, sb = M.moe_quant_weight_fp8(b.to(dev()))
+    qao, sao = OC.quant_fp8_act(a.numpy())
+    qbo, sbo = OC.quant_fp8_weight(b.numpy())
+    np.testing.assert_array_equal(to_np(qa), qao)
+    np.testing.assert_array_equal(to_np(qb), qbo)
+    off_d = torch.from_numpy(offsets).to(dev())
+    ref = O.grouped_gemm_fp8(qao, sao, qbo, sbo, offsets)
+    live = np.zeros(R, bool)
+    for g in range(len(sizes)):
+        live[offsets[g]:offsets[g] + sizes[g]] = True
+    if not swiglu:
+        c = M.grouped_gemm_fp8(qa, sa, qb, sb, off_d, R, N)
+        beyond, raw = error_ratios(to_np(c)[live], ref[live])
+        print(f"beyond={beyond:.3e} raw={raw:.3e}")
+        assert beyond <= TOL
+    else:
+        codes, sc = M.grouped_gemm_fp8(qa, sa, qb, sb, off_d, R, N, swiglu=True)
+        A = OC.dequant_fp8_act(qao, sao)
+        Bd = OC.dequant_fp8_weight(qbo, sbo)
+        sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)      # sum_k |a_k b_k|
+        h, dh = swiglu_error_model(ref[:, :N], ref[:, N:], sab[:, :N], sab[:, N:])
+        q, s, q_lo, q_hi, delta, rho = requant_band(h[live], dh[live])
+        qg, sg = to_np(codes)[live], to_np(sc)[live]
+        # the GPU scale is fl32(amax/448) of its own h: within the amax error band
+        assert np.all(np.abs(sg.astype(np.float64) - s) <= s * rho * 1.01)
+        dg = OC.e4m3_decode(qg)
+        ok = (dg >= np.minimum(OC.e4m3_decode(q_lo), OC.e4m3_decode(q_hi))) & \
+             (dg <= np.maximum(OC.e4m3_decode(q_lo), OC.e4m3_decode(q_hi)))
+        unique = q_lo == q_hi
+        print(f"unambiguous codes {unique.mean():.6f}, all codes valid {ok.mean():.6f}")
+        # where the rounding is unambiguous the code is bit-exact; elsewhere it is one
+        # of the correct neighbours
+        np.testing.assert_array_equal(qg[unique], q[unique])
+        assert ok.all()
+
+
+def test_grouped_gemm_fp8_row_gather():
+    """GEMM1's activation gather: logical row r reads A row a_rows[r] // div."""
+    note("gemm fp8 gather")
+    T, k, E, N, K = 50, 2, 4, 128, 256
+    idx = synth.random_topk(T, E, k, seed=4)
+    counts, offsets, ros, sor = O.dispatch(idx, E, 16)
+    x = synth.normal((T, K), 12, "x", dtype=torch.bfloat16)
+    w = synth.normal((E, N, K), 12, "w13", std=K ** -0.5)
+    qx, sx = M.moe_quant_fp8(x.to(dev()))
+    qw, sw = M.moe_quant_weight_fp8(w.to(dev()))
+    R = len(sor)
+    c = M.grouped_gemm_fp8(qx, sx, qw, sw, torch.from_numpy(offsets).to(dev()), R, N,
+                           a_rows=torch.from_numpy(sor).to(dev()), a_row_div=k)
+    qxo, sxo = OC.quant_fp8_act(x.float().numpy())
+    qwo, swo = OC.quant_fp8_weight(w.numpy())
+    live = sor >= 0
+    A = np.zeros((R, K), np.uint8)
+    sA = np.ones((R, K // 128), np.float32)
+    A[live] = qxo[sor[live] // k]
+    sA[live] = sxo[sor[live] // k]
+    ref = O.grouped_gemm_fp8(A, sA, qwo, swo, offsets)
+    beyond, raw = error_ratios(to_np(c)[live], ref[live])
+    assert beyond <= TOL
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_w4a16(swiglu):
+    sizes = [70, 0, 130, 5]
+    N, K = 128, 256
+    note(f"gemm w4a16 swiglu={swiglu}")
+    a, b, offsets, R = _gemm_case(sizes, N, K, 16, 13, swiglu)
+    a_bf = a.to(torch.bfloat16)
+    qb, s7 = M.moe_quant_weight_int4(b.to(dev()))
+    qbo, s7o = OC.int4_quant_rows(b.numpy())
+    np.testing.assert_array_equal(to_np(qb), OC.int4_pack(qbo))
+    c = M.grouped_gemm_w4a16(a_bf.to(dev()), qb, s7, torch.from_numpy(offsets).to(dev()), R, N,
+                             swiglu=swiglu)
+    ref = O.grouped_gemm(a_bf.float().numpy(), OC.int4_dequant(qbo, s7o), offsets)
+    live = np.zeros(R, bool)
+    for g in range(len(sizes)):
+        live[offsets[g]:offsets[g] + sizes[g]] = True
+    if swiglu:
+        ref = O.swiglu(ref[:, :N], ref[:, N:])
+    beyond, raw = error_ratios(to_np(c)[live], ref[live])
+    print(f"beyond={beyond:.3e} raw={raw:.3e}")
+    assert beyond <= TOL
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_f32(swiglu):
+    sizes = [30, 0, 19, 64]
+    N, K = 96, 200
+    note(f"gemm f32 swiglu={swiglu}")
+    rng = np.random.default_rng(1)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(offsets[-1])
+    a = rng.standard_normal((R, K)).astype(np.float32)
+    b = (rng.standard_normal((4, 2 * N if swiglu else N, K)) / np.sqrt(K)).astype(np.float32)
+    c = M.grouped_gemm_f32(torch.from_numpy(a).to(dev()), torch.from_numpy(b).to(dev()),
+                           torch.from_numpy(offsets).to(dev()), R, N, swiglu=swiglu)
+    ref = O.grouped_gemm(a, b, offsets)
+    if swiglu:
+        ref = O.swiglu(ref[:, :N], ref[:, N:])
+    beyond, raw = error_ratios(to_np(c), ref, rounding=0.0)
+    assert raw <= TOL
+
+
+@pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32])
+def test_combine(o_dtype):
+    note(f"combine {o_dtype}")
+    T, k, E, d = 99, 4, 16, 256
+    idx = synth.random_topk(T, E, k, seed=5)
+    _, offsets, ros, sor = O.dispatch(idx, E, 8, cap=20)
+    R = len(sor)
+    o = synth.normal((R, d), 14, "x", dtype=o_dtype)
+    w = synth.uniform((T, k), 0, 1, 14, "bias")
+    y = M.moe_combine(o.to(dev()), torch.from_numpy(ros).to(dev()), w.to(dev()), T, k, o_dtype)
+    ref = O.combine(o.float().numpy(), ros, w.numpy(), T, k)
+    if o_dtype == torch.bfloat16:
+        beyond, raw = error_ratios(to_np(y), ref)
+        assert beyond <= 1e-5
+    else:
+        beyond, raw = error_ratios(to_np(y), ref, rounding=0.0)
+        assert raw <= 1e-5
+
+
+def test_determinism():
+    note("determinism")
+    a, b, offsets, R = _gemm_case([200, 3, 77], 256, 512, 16, 15, True)
+    qa, sa = M.moe_quant_fp8(a.to(dev()))
+    qb, sb = M.moe_quant_weight_fp8(b.to(dev()))
+    off = torch.from_numpy(offsets).to(dev())
+    c1, s1 = M.grouped_gemm_fp8(qa, sa, qb, sb, off, R, 256, swiglu=True)
+    c2, s2 = M.grouped_gemm_fp8(qa, sa, qb, sb, off, R, 256, swiglu=True)
+    live = np.zeros(R, bool)
+    live[:offsets[-1]] = True
+    assert torch.equal(c1[:offsets[-1]], c2[:offsets[-1]])
+    assert torch.equal(s1[:offsets[-1]], s2[:offsets[-1]])
