@@ -27,6 +27,8 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the promotion FMAs read them without accvgpr moves
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"),
 ]
 

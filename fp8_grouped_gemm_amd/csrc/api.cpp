@@ -68,10 +68,13 @@ int hip_status(hipError_t e, const char* what) {
 
 inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
+// Rows per GEMM tile from the average rows per group: decode-sized groups use 16-row
+// tiles; otherwise 128-row tiles, whose padding rows cost neither fetches nor MFMAs.
 int pick_bm(double avg_rows, bool swiglu) {
+  (void)swiglu;
   if (avg_rows <= 16) return 16;
-  if (avg_rows <= 48) return 32;
-  if (swiglu || avg_rows <= 96) return 64;
+  if (avg_rows <= 32) return 32;
+  if (avg_rows <= 64) return 64;
   return 128;
 }
 

@@ -64,4 +64,10 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// silu with a hardware reciprocal (about 1 ulp) in place of the IEEE division; used in
+// GEMM epilogues whose result is rounded to 8 bits right after.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 }  // namespace moe

@@ -14,11 +14,15 @@
 //   * v_mfma_f32_16x16x128_f8f6f4: one instruction covers one 16x16 output tile over
 //     exactly one 128-deep scale block, so promotion is one fp32 FMA per output per
 //     block: acc += (sA*sB) * mfma(a, b, 0).
-//   * 256 threads = 4 wave64s; workgroup tile BM x 128 output columns; a SwiGLU tile
+//   * 256 threads = 4 wave64s over a BM x BNB tile (BNB rows of B).  Prefill tiles are
+//     128 x 256 with 64 x 128 per wave, so one weight byte brought into LDS feeds 128
+//     token rows and every fragment read from LDS feeds 4 or 8 MFMAs.  A SwiGLU tile
 //     loads 128 gate rows and 128 up rows of B so the 1x128 requant block is complete
 //     inside one workgroup.
-//   * Operands are staged through LDS with a 16-byte XOR swizzle (row stride 128 B);
-//     the next K block is fetched into registers while the current one is multiplied.
+//   * Operands reach LDS by direct global->LDS DMA into 3 buffers (two K blocks in
+//     flight), in a 16-byte XOR swizzle (row stride 128 B) read back conflict-free.
+//     Row groups past the end of the group are not fetched and waves whose rows are all
+//     padding skip their MFMAs, so small groups cost little more than their weights.
 //   * Persistent grid: workgroup b works on tiles v, v+P, v+2P, ... where
 //     v = (b mod 8) * P/8 + b/8, so consecutive tiles -- the row tiles that share one
 //     B column tile -- run on the same XCD and share its L2.
@@ -71,58 +75,69 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// BM rows x 128 output columns per tile.  SWIGLU: B tile = 128 gate + 128 up rows.
-//
-// K loop: NS = 3 LDS stages filled by direct global->LDS DMA (16 bytes per lane), two
-// K blocks in flight while the third is multiplied.  Every wave issues the same number
-// of DMA instructions per stage (A rows, B rows, one 64-lane scale load), so one
-// s_waitcnt vmcnt per stage plus a barrier publishes the stage to all waves.
-template <int BM, bool SWIGLU>
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  // s_waitcnt needs an immediate: dispatch a runtime count in [0, N]
+  if constexpr (N > 0) {
+    if (n >= N) { wait_vmcnt<N>(); return; }
+    wait_vmcnt_upto<N - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// Two tile classes share one persistent tile list: groups with at most BMS rows are
+// cut into BMS-row tiles worked by 4 waves side by side (all SIMDs busy, the weight
+// stream dominates), larger groups into 128-row tiles worked by 2 x 2 waves (a weight
+// byte in LDS feeds 128 rows).  B tile: BNB rows (SWIGLU: BNB/2 gate + BNB/2 up rows ->
+// BNB/2 output columns; plain: BNB output columns).
+template <int BMS, int BNB, bool SWIGLU>
 __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
   constexpr int NS = 3;
-  constexpr int BN = 128;                         // output columns per tile
-  constexpr int BNB = SWIGLU ? 2 * BN : BN;       // B rows per tile
-  constexpr int WM = (BM >= 128) ? 2 : 1;         // wave grid
-  constexpr int WN = 4 / WM;
-  constexpr int WTM = BM / WM;                    // rows per wave
-  constexpr int TM = WTM / 16;                    // 16-row MFMA tiles per wave
-  constexpr int WCOL = BN / WN;                   // output columns per wave
-  constexpr int TN = (SWIGLU ? 2 : 1) * WCOL / 16;  // 16-col MFMA tiles per wave
-  constexpr int AR = BM < 32 ? 32 : BM;           // A rows loaded (BM 16: two copies)
-  constexpr int A_IN = AR / 32;                   // DMA instructions per wave: A
-  constexpr int B_IN = BNB / 32;                  //                            B
-  constexpr int PER = A_IN + B_IN + 1;            //                 + one scale load
-  constexpr int A_BYTES = AR * 128, B_BYTES = BNB * 128;
-  constexpr int SC_OFF = A_BYTES + B_BYTES;       // 4 x 256 B of scale slots
+  constexpr int BMB = 128;                         // rows of a big-group tile
+  constexpr int BN_OUT = SWIGLU ? BNB / 2 : BNB;   // output columns per tile
+  constexpr int B_IN = BNB / 32;                   // B DMA instructions per wave
+  constexpr int A_IN_MAX = BMB / 32;
+  constexpr int PER_MAX = A_IN_MAX + B_IN + 1;     // + one scale load
+  constexpr int A_BYTES = BMB * 128, B_BYTES = BNB * 128;
+  constexpr int SC_OFF = A_BYTES + B_BYTES;        // 4 x 256 B of scale slots
   constexpr int STAGE = SC_OFF + 1024;
-  static_assert(TM >= 1 && WCOL % 16 == 0, "tile shape");
-  static_assert(PER < 16, "vmcnt encoding");
+  static_assert(!SWIGLU || BN_OUT == 128, "1x128 requant block");
+  static_assert(PER_MAX < 16, "vmcnt encoding");
 
   __shared__ TileMap tm;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS][STAGE];
-  __shared__ float red[SWIGLU ? WN : 1][SWIGLU ? BM : 1];
+  __shared__ float red[SWIGLU ? 4 : 1][SWIGLU ? BMB : 1];
   __shared__ int row_src[128];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / WN, wn = wid % WN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = args.G, K = args.K, N = args.N, KB = K / 128;
-  const int tiles_n = N / BN;
+  const int tiles_n = N / BN_OUT;
 
-  build_tile_map<BM>(tm, args.offsets, G);
+  build_tile_map<BMS, BMB>(tm, args.offsets, G);
   const int total = tm.start[G] * tiles_n;
   const int P = gridDim.x;
   const int b = blockIdx.x;
   const int v = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
+  const uint32_t lds0 = lds_addr(&lds[0][0]);
+  const int lr8 = lane >> 3, slot = lane & 7, piece = slot ^ lr8;
+  const int gsel = 2 * (lane >> 4);
 
-  for (int t = v; t < total; t += P) {
-    // ---- locate the tile
-    const int g = find_group(tm, G, t, tiles_n);
-    const int mt = tm.start[g + 1] - tm.start[g];
-    const int local = t - tm.start[g] * tiles_n;
-    const int ni = local / mt, mi = local % mt;
-    const int row0 = tm.off[g] + mi * BM;
-    const int row_end = tm.off[g + 1];
-    const int n0 = ni * BN;
+  // one tile of class BM (WM waves along M)
+  auto run_tile = [&](auto BMC, int g, int row0, int row_end, int n0) {
+    constexpr int BM = decltype(BMC)::value;
+    constexpr int WM = BM == BMB ? 2 : 1;
+    constexpr int WN = 4 / WM;
+    constexpr int WTM = BM / WM;                   // rows per wave
+    constexpr int TM = WTM / 16;                   // 16-row MFMA tiles per wave
+    constexpr int WTN = BNB / WN;                  // B rows per wave
+    constexpr int TN = WTN / 16;                   // 16-col MFMA tiles per wave
+    constexpr int AR = BM < 32 ? 32 : BM;          // A rows in LDS (BM 16: rows repeat)
+    constexpr int A_IN = AR / 32;                  // A DMA instructions per wave
+    static_assert(TM >= 1 && TN >= 2 && TN % 2 == 0, "tile shape");
+    const int wm = wid / WN, wn = wid % WN;
+    const int n_valid = min(row_end - row0, BM);   // >= 1
 
     // source row of every tile row (gather through a_rows); rows past the group's end
     // repeat its last row, their results are discarded
@@ -140,46 +155,45 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
     // ---- this lane's DMA sources.  A wave instruction fills 1024 LDS bytes = 8 rows
     // of 128 B; lane L lands at row L/8, slot L%8 and fetches global piece
     // (L%8) ^ (row%8), which realises the XOR swizzle read back below.
-    const int lr8 = lane >> 3, slot = lane & 7, piece = slot ^ lr8;
     const uint8_t* a_src[A_IN];
 #pragma unroll
     for (int i = 0; i < A_IN; ++i) {
-      const int row = (wid * A_IN + i) * 8 + lr8;              // 0 .. AR-1
+      const int row = (wid * A_IN + i) * 8 + lr8;               // 0 .. AR-1
       a_src[i] = args.A + (size_t)row_src[row % BM] * K + piece * 16;
     }
+    // A row groups holding at least one real row; the rest are never fetched
+    const int a_cnt = min(max((min(n_valid, AR) - wid * A_IN * 8 + 7) / 8, 0), A_IN);
+    const int per = a_cnt + B_IN + 1;               // DMA instructions per stage
     const size_t nbrows = SWIGLU ? 2 * (size_t)N : (size_t)N;
     const uint8_t* b_src[B_IN];
 #pragma unroll
     for (int i = 0; i < B_IN; ++i) {
-      const int row = (wid * B_IN + i) * 8 + lr8;              // 0 .. BNB-1
-      const int grow = SWIGLU ? (row < BN ? n0 + row : N + n0 + row - BN) : n0 + row;
+      const int row = (wid * B_IN + i) * 8 + lr8;               // 0 .. BNB-1
+      const int grow = SWIGLU ? (row < BN_OUT ? n0 + row : N + n0 + row - BN_OUT) : n0 + row;
       b_src[i] = args.B + ((size_t)g * nbrows + grow) * K + piece * 16;
     }
-    // scale DMA: wave 0 -> sA rows 0..63, wave 1 -> sA rows 64..127, wave 2 -> sB
-    // (lanes < 32 gate block, >= 32 up block), wave 3 -> a spare copy of sB
+    // scale DMA: waves 0/1 -> sA rows 0..63 / 64..127; waves 2/3 -> sB, lanes < 32 the
+    // first B column block of the tile, lanes >= 32 the second (SwiGLU: gate / up)
     const size_t nbk = nbrows / 128;
     const float* sc_src;
     if (wid < 2) {
       sc_src = args.sA + (size_t)row_src[(wid * 64 + lane) % BM] * KB;
     } else {
-      const int nb = (SWIGLU && lane >= 32) ? (N + n0) / 128 : n0 / 128;
+      int nb = n0 / 128;
+      if (lane >= 32) nb = SWIGLU ? (N + n0) / 128 : min(n0 / 128 + 1, (int)nbk - 1);
       sc_src = args.sB + ((size_t)g * nbk + nb) * KB;
     }
-
-    // wave-uniform LDS byte address of this wave's first DMA slot in stage 0
-    const uint32_t m_wave = __builtin_amdgcn_readfirstlane(lds_addr(&lds[0][0]) +
-                                                           (uint32_t)wid * (A_IN * 1024));
-    const uint32_t mb_wave = __builtin_amdgcn_readfirstlane(lds_addr(&lds[0][0]) + A_BYTES +
-                                                            (uint32_t)wid * (B_IN * 1024));
-    const uint32_t ms_wave = __builtin_amdgcn_readfirstlane(lds_addr(&lds[0][0]) + SC_OFF +
-                                                            (uint32_t)wid * 256);
+    const uint32_t m_a = lds0 + (uint32_t)wid * (A_IN * 1024);
+    const uint32_t m_b = lds0 + A_BYTES + (uint32_t)wid * (B_IN * 1024);
+    const uint32_t m_s = lds0 + SC_OFF + (uint32_t)wid * 256;
     auto issue = [&](int st, int kb) {
       const uint32_t so = (uint32_t)st * STAGE;
 #pragma unroll
-      for (int i = 0; i < A_IN; ++i) dma16(a_src[i] + (size_t)kb * 128, m_wave + so + i * 1024);
+      for (int i = 0; i < A_IN; ++i)
+        if (i < a_cnt) dma16(a_src[i] + (size_t)kb * 128, m_a + so + i * 1024);
 #pragma unroll
-      for (int i = 0; i < B_IN; ++i) dma16(b_src[i] + (size_t)kb * 128, mb_wave + so + i * 1024);
-      dma4(sc_src + kb, ms_wave + so);
+      for (int i = 0; i < B_IN; ++i) dma16(b_src[i] + (size_t)kb * 128, m_b + so + i * 1024);
+      dma4(sc_src + kb, m_s + so);
     };
 
     v4f acc[TM][TN];
@@ -187,118 +201,106 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    const bool active = wm * WTM < n_valid;          // wave has a real row
 
-    // operand fragments of one K block, double-buffered in registers: the block after
-    // the current one is read from LDS while the current one is multiplied
-    const int gsel = 2 * (lane >> 4);
-    v8i af[2][TM], bfr[2][TN];
-    v4f sa[2][TM];
-    float sb0[2], sb1[2];
-    // buffer indices are compile-time constants so the fragments stay in registers
-    auto read_frags = [&](auto BUF, int stg) {
-      constexpr int buf = decltype(BUF)::value;
-      const uint8_t* L = lds[stg];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WTM + i * 16 + (lane & 15);
-        const uint8_t* base = L + row * 128;
-        const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ (row & 7)) << 4));
-        const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ (row & 7)) << 4));
-        af[buf][i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        int brow;
-        if (SWIGLU) {
-          const int half = j / (TN / 2), jj = j % (TN / 2);
-          brow = half * BN + wn * WCOL + jj * 16 + (lane & 15);
-        } else {
-          brow = wn * WCOL + j * 16 + (lane & 15);
-        }
-        const uint8_t* base = L + A_BYTES + brow * 128;
-        const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ (brow & 7)) << 4));
-        const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ (brow & 7)) << 4));
-        bfr[buf][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      const float* lsa = reinterpret_cast<const float*>(L + SC_OFF);
-      const float* lsb = reinterpret_cast<const float*>(L + SC_OFF + 512);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        sa[buf][i] = *reinterpret_cast<const v4f*>(&lsa[wm * WTM + i * 16 + (lane >> 4) * 4]);
-      sb0[buf] = lsb[0];
-      sb1[buf] = lsb[32];
-    };
-
-    // Pipeline: stages kb+1 and kb+2 are in flight (DMA) while block kb is multiplied
-    // from registers and block kb+1 is read from LDS into the other register set.  The
-    // K loop is unrolled by two so the register set of every block is static.
+    // K loop: buffers hold blocks kb, kb+1, kb+2 (NS = 3); while block kb is
+    // multiplied, kb+1 and kb+2 are in flight.  One barrier per block: it publishes
+    // block kb and certifies every wave is done with block kb-1, whose buffer is refilled.
     issue(0, 0);
     if (KB > 1) issue(1, 1);
-    if (KB > 2) issue(2, 2);
-    if (KB > 2) wait_vmcnt<2 * PER>(); else if (KB > 1) wait_vmcnt<PER>(); else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    read_frags(std::integral_constant<int, 0>{}, 0);
-    int st = 0;  // stage of block kb
-    auto kstep = [&](int kb, auto CUR) {
-      constexpr int cur = decltype(CUR)::value;
-      const int st1 = st == NS - 1 ? 0 : st + 1;   // stage of block kb+1
-      // block kb's fragments are in registers; every wave must be done reading stage
-      // st before it is refilled, and block kb+1 must have landed in stage st1
-      __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
-      if (kb + 2 < KB) wait_vmcnt<PER>(); else wait_vmcnt<0>();
+    int st = 0;
+    for (int kb = 0; kb < KB; ++kb) {
+      wait_vmcnt_upto<PER_MAX>(kb + 1 < KB ? per : 0);
       __builtin_amdgcn_s_barrier();
-      if (kb + 3 < KB) issue(st, kb + 3);
-      if (kb + 1 < KB) read_frags(std::integral_constant<int, cur ^ 1>{}, st1);
-
-      const v4f zero = {0.f, 0.f, 0.f, 0.f};
-      v4f s0[TM], s1[TM];
+      if (kb + 2 < KB) issue(st == 0 ? 2 : st - 1, kb + 2);    // buffer (kb+2) % 3
+      if (active) {
+        const uint8_t* L = lds[st];
+        const float* lsa = reinterpret_cast<const float*>(L + SC_OFF);
+        const float* lsb = reinterpret_cast<const float*>(L + SC_OFF + 512);
+        v8i af[TM];
+        auto read_a = [&](int i) {
+          const int row = wm * WTM + i * 16 + (lane & 15);
+          const uint8_t* base = L + row * 128;
+          const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ (row & 7)) << 4));
+          const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ (row & 7)) << 4));
+          af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        auto read_b = [&](int j) {
+          int brow;
+          if (SWIGLU) {
+            const int half = j / (TN / 2), jj = j % (TN / 2);
+            brow = half * BN_OUT + wn * (WTN / 2) + jj * 16 + (lane & 15);
+          } else {
+            brow = wn * WTN + j * 16 + (lane & 15);
+          }
+          const uint8_t* base = L + A_BYTES + brow * 128;
+          const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ (brow & 7)) << 4));
+          const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ (brow & 7)) << 4));
+          return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        // promotion scales: sA of this lane's 4 rows per row tile times sB of the
+        // column block (plain: this wave's block; SwiGLU: gate for j < TN/2, up after)
+        const float sbA = SWIGLU ? lsb[0] : lsb[wn * WTN >= 128 ? 32 : 0];
+        const float sbB = lsb[32];
+        v4f sa[TM];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        s0[i] = sa[cur][i] * sb0[cur];
-        s1[i] = sa[cur][i] * sb1[cur];
-      }
-      // MFMA t into one partial while the previous partial is promoted
-      v4f p[2];
+        for (int i = 0; i < TM; ++i)
+          sa[i] = *reinterpret_cast<const v4f*>(&lsa[wm * WTM + i * 16 + (lane >> 4) * 4]);
+        // the A fragments stay in registers; B column tiles stream through two register
+        // sets, the next one read while the current one is multiplied
+        v8i bcur = read_b(0);
 #pragma unroll
-      for (int t = 0; t <= TM * TN; ++t) {
-        if (t < TM * TN) {
-          const int i = t / TN, j = t % TN;
-          p[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[cur][i], bfr[cur][j],
-                                                                     zero, 0, 0, 0, 0, 0, 0);
+        for (int i = 0; i < TM; ++i) read_a(i);
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const v8i bnext = (j + 1 < TN) ? read_b(j + 1) : bcur;
+          const float sb = (SWIGLU && j >= TN / 2) ? sbB : sbA;
+          v4f pp[TM];
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            pp[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bcur, zero, 0, 0, 0,
+                                                                    0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const v4f sc = sa[i] * sb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc[r], pp[i][r], acc[i][j][r]);
+          }
+          bcur = bnext;
         }
-        if (t > 0) {
-          const int i = (t - 1) / TN, j = (t - 1) % TN;
-          const v4f sc = (SWIGLU && j >= TN / 2) ? s1[i] : s0[i];
-          const v4f q = p[(t - 1) & 1];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc[r], q[r], acc[i][j][r]);
-        }
       }
-      st = st1;
-    };
-    int kb = 0;
-    for (; kb + 1 < KB; kb += 2) {
-      kstep(kb, std::integral_constant<int, 0>{});
-      kstep(kb + 1, std::integral_constant<int, 1>{});
+      st = st == NS - 1 ? 0 : st + 1;
     }
-    if (kb < KB) kstep(kb, std::integral_constant<int, 0>{});
 
-    // ---- epilogue.  MFMA C layout: lane holds column lane%16, rows 4*(lane/16)+r.
+    // ---- epilogue.  MFMA C layout: lane holds column lane%16, rows 4*(lane/16)+r.  The
+    // tile is staged through LDS (every DMA has landed, the stage buffers are free) so
+    // that global stores are 16 contiguous bytes per lane.
+    uint8_t* ot = &lds[0][0];
     if constexpr (!SWIGLU) {
-      uint16_t* C = static_cast<uint16_t*>(args.C);
+      constexpr int OB = BNB * 2;                    // bytes per staged row
+      __syncthreads();
+      if (active) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = row0 + wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-          if (row < row_end) {
+          for (int r = 0; r < 4; ++r) {
+            const int trow = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-              const int col = n0 + wn * WCOL + j * 16 + (lane & 15);
-              C[(size_t)row * N + col] = f32_to_bf16(acc[i][j][r]);
+              const int tcol = wn * WTN + j * 16 + (lane & 15);
+              *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(acc[i][j][r]);
             }
           }
-        }
+      }
+      __syncthreads();
+      uint8_t* C = static_cast<uint8_t*>(args.C);
+      constexpr int CPR = OB / 16;                   // 16-byte chunks per row
+      for (int c = tid; c < n_valid * CPR; c += 256) {
+        const int trow = c / CPR, ch = c % CPR;
+        *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) =
+            *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
+      }
     } else {
       constexpr int TH = TN / 2;
       float h[TM][TH][4];
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
           float m = 0.f;
 #pragma unroll
           for (int j = 0; j < TH; ++j) {
-            h[i][j][r] = silu(acc[i][j][r]) * acc[i][j + TH][r];
+            h[i][j][r] = silu_fast(acc[i][j][r]) * acc[i][j + TH][r];
             m = fmaxf(m, fabsf(h[i][j][r]));
           }
           rmax[i][r] = group_max<16>(m);  // across the 16 columns of the MFMA tile
@@ -323,64 +325,92 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
             red[wn][wm * WTM + i * 16 + (lane >> 4) * 4 + r] = rmax[i][r];
       }
       __syncthreads();
-      uint8_t* C = static_cast<uint8_t*>(args.C);
+      if (active) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int trow = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-          float m = red[0][trow];
+          for (int r = 0; r < 4; ++r) {
+            const int trow = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
+            float m = red[0][trow];
 #pragma unroll
-          for (int w = 1; w < WN; ++w) m = fmaxf(m, red[w][trow]);
-          const float s = block_scale(m);
-          const int row = row0 + trow;
-          if (row < row_end) {
+            for (int w = 1; w < WN; ++w) m = fmaxf(m, red[w][trow]);
+            const float s = block_scale(m);
+            const float inv = 1.0f / s;
 #pragma unroll
             for (int j = 0; j < TH; ++j) {
-              const int col = n0 + wn * WCOL + j * 16 + (lane & 15);
-              C[(size_t)row * N + col] = (uint8_t)(e4m3x2(clamp448(h[i][j][r] / s), 0.f) & 0xFF);
+              const int tcol = wn * (WTN / 2) + j * 16 + (lane & 15);
+              ot[trow * 128 + tcol] = (uint8_t)(e4m3x2(clamp448(h[i][j][r] * inv), 0.f) & 0xFF);
             }
-            if (wn == 0 && (lane & 15) == 0) args.sC[(size_t)row * (N / 128) + n0 / 128] = s;
+            const int row = row0 + trow;
+            if (wn == 0 && (lane & 15) == 0 && row < row_end)
+              args.sC[(size_t)row * (N / 128) + n0 / 128] = s;
           }
-        }
+      }
+      __syncthreads();
+      uint8_t* C = static_cast<uint8_t*>(args.C);
+      for (int c = tid; c < n_valid * 8; c += 256) {
+        const int trow = c / 8, ch = c % 8;
+        *reinterpret_cast<v4i*>(C + (size_t)(row0 + trow) * N + n0 + ch * 16) =
+            *reinterpret_cast<const v4i*>(ot + trow * 128 + ch * 16);
+      }
     }
     __syncthreads();  // LDS (row_src, red, stages) is reused by the next tile
+  };
+
+  for (int t = v; t < total; t += P) {
+    // ---- locate the tile
+    const int g = find_group(tm, G, t, tiles_n);
+    const int mt = tm.start[g + 1] - tm.start[g];
+    const int local = t - tm.start[g] * tiles_n;
+    const int ni = local / mt, mi = local % mt;
+    const int rows = tm.off[g + 1] - tm.off[g];
+    const int n0 = ni * BN_OUT;
+    if (rows <= BMS)
+      run_tile(std::integral_constant<int, BMS>{}, g, tm.off[g] + mi * BMS, tm.off[g + 1], n0);
+    else
+      run_tile(std::integral_constant<int, BMB>{}, g, tm.off[g] + mi * BMB, tm.off[g + 1], n0);
   }
 }
-
-static int g_num_cus = 0;
 
 hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows, int a_row_div,
                            const uint8_t* B, const float* sB, const int32_t* offsets, int G,
                            int R_cap, int N, int K, bool swiglu, void* C, float* sC, int bm,
                            int num_cus, hipStream_t s) {
   GemmArgs a{A, sA, a_rows, a_row_div, B, sB, offsets, G, N, K, C, sC};
-  const long tiles_n = N / 128;
-  const long mtiles = R_cap / bm + G;
+  const bool wide = !swiglu && N % 256 == 0;      // 256 output columns per plain tile
+  const long tiles_n = swiglu ? N / 128 : (wide ? N / 256 : N / 128);
+  const long mtiles = R_cap / (bm < 128 ? bm : 64) + G;
   long grid = std::min<long>(mtiles * tiles_n, (long)num_cus);
   if (grid >= 8) grid = grid / 8 * 8;
   if (grid < 1) grid = 1;
   dim3 gd((unsigned)grid), bd(256);
-#define MOE_GEMM_CASE(BMV, SW)                                                   \
-  hipLaunchKernelGGL((gemm_fp8_kernel<BMV, SW>), gd, bd, 0, s, a);
+  // bm: tile rows of small groups (16, 32 or 64); groups above it use 128-row tiles
+  const int bms = bm >= 64 ? 64 : bm;
+#define MOE_GEMM_CASE(BMSV, BNBV, SW) \
+  hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, BNBV, SW>), gd, bd, 0, s, a)
   if (swiglu) {
-    switch (bm) {
-      case 16: MOE_GEMM_CASE(16, true); break;
-      case 32: MOE_GEMM_CASE(32, true); break;
-      case 64: MOE_GEMM_CASE(64, true); break;
+    switch (bms) {
+      case 16: MOE_GEMM_CASE(16, 256, true); break;
+      case 32: MOE_GEMM_CASE(32, 256, true); break;
+      case 64: MOE_GEMM_CASE(64, 256, true); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (wide) {
+    switch (bms) {
+      case 16: MOE_GEMM_CASE(16, 256, false); break;
+      case 32: MOE_GEMM_CASE(32, 256, false); break;
+      case 64: MOE_GEMM_CASE(64, 256, false); break;
       default: return hipErrorInvalidValue;
     }
   } else {
-    switch (bm) {
-      case 16: MOE_GEMM_CASE(16, false); break;
-      case 32: MOE_GEMM_CASE(32, false); break;
-      case 64: MOE_GEMM_CASE(64, false); break;
-      case 128: MOE_GEMM_CASE(128, false); break;
+    switch (bms) {
+      case 16: MOE_GEMM_CASE(16, 128, false); break;
+      case 32: MOE_GEMM_CASE(32, 128, false); break;
+      case 64: MOE_GEMM_CASE(64, 128, false); break;
       default: return hipErrorInvalidValue;
     }
   }
 #undef MOE_GEMM_CASE
-  (void)g_num_cus;
   return hipGetLastError();
 }
 

@@ -19,7 +19,11 @@ struct TileMap {
   int off[kMaxGroups + 1];    // copy of offsets
 };
 
-template <int BM>
+// Rows per tile of a group with M rows: BMS for small groups (M <= BMS), BMB otherwise.
+template <int BMS, int BMB>
+__device__ __forceinline__ int tile_rows(int M) { return M <= BMS ? BMS : BMB; }
+
+template <int BMS, int BMB = BMS>
 __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int G) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   __shared__ int wsum[4];
@@ -29,7 +33,11 @@ __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets,
   const int per = (G + 255) / 256;
   const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
   int local = 0;
-  for (int g = g0; g < g1; ++g) local += (tm.off[g + 1] - tm.off[g] + BM - 1) / BM;
+  for (int g = g0; g < g1; ++g) {
+    const int M = tm.off[g + 1] - tm.off[g];
+    const int bm = tile_rows<BMS, BMB>(M);
+    local += (M + bm - 1) / bm;
+  }
   int incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -43,7 +51,9 @@ __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets,
   int run = base + incl - local;
   for (int g = g0; g < g1; ++g) {
     tm.start[g] = run;
-    run += (tm.off[g + 1] - tm.off[g] + BM - 1) / BM;
+    const int M = tm.off[g + 1] - tm.off[g];
+    const int bm = tile_rows<BMS, BMB>(M);
+    run += (M + bm - 1) / bm;
   }
   if (tid == 255) tm.start[G] = base + incl;
   __syncthreads();
