@@ -158,16 +158,32 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_fp8", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default="prefill_fp8",
+                    choices=sorted(synth.WORKLOADS) + ["grouped_gemm_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print a per-kernel summary of a rocprofv3 --kernel-trace --stats "
+                         "--output-format csv run written to DIR, then exit")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="print per-kernel average counter values of a rocprofv3 --pmc "
+                         "--output-format csv run written to DIR, then exit")
     a = ap.parse_args(argv)
+    if a.trace_summary:
+        print(trace_summary(a.trace_summary))
+        return 0
+    if a.pmc_summary:
+        print(json.dumps(pmc_summary(a.pmc_summary), indent=1))
+        return 0
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
                                    "(multi-GPU expert parallelism is not built)"}))
         return 2
 
     import fp8_grouped_gemm_amd as M
+    if a.workload == "grouped_gemm_fp8":
+        print(json.dumps(bench_grouped_gemm(M, a.steps, a.warmup)), flush=True)
+        return 0
     w = synth.WORKLOADS[a.workload]
     if w.mode == "fp8" and a.workload == "prefill_fp8":
         w = synth.scaled(w, m_align=16)
@@ -210,12 +226,13 @@ def main(argv=None):
         log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
     g1_ms = stages.get("gemm1")
     roofline = None
+    traffic = measured_traffic("gemm1") if a.workload == "prefill_fp8" else None
     if g1_ms:
         achieved = g["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9
         roofline = {"kernel": "grouped_gemm_fp8 (GEMM1: gate+up, SwiGLU, e4m3 requant)",
                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": None, "avg_ms": round(g1_ms, 4),
+                    "traffic": traffic, "avg_ms": round(g1_ms, 4),
                     "tflops": round(g["gemm1_flops"] / (g1_ms * 1e-3) / 1e12, 1),
                     "bytes_per_launch": g["gemm1_bytes"]}
     out = {
@@ -240,6 +257,101 @@ def main(argv=None):
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of a GEMM kernel from the committed rocprofv3 counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_fp8_prefill_traffic.json")
+    src = os.path.join(ROOT, "fp8_grouped_gemm_amd", "csrc", "gemm_fp8.hip")
+    try:
+        d = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256") != sha:
+        return None
+    return round(d[kernel]["hbm_bytes_per_launch"])
+
+
+def _find(dirname, suffix):
+    for root, _, files in os.walk(dirname):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {dirname}")
+
+
+def trace_summary(dirname):
+    """Per-kernel call count and average / total duration from rocprofv3's kernel
+    stats csv (library kernels first)."""
+    import csv
+    rows = list(csv.DictReader(open(_find(dirname, "kernel_stats.csv"))))
+    out = [f"{'kernel':<72} {'calls':>6} {'avg_us':>10} {'total_ms':>10} {'pct':>6}"]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 70:
+            name = name[:67] + "..."
+        out.append(f"{name:<72} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                   f"{float(r['TotalDurationNs']) / 1e6:>10.3f} {float(r['Percentage']):>6.2f}")
+    return "\n".join(out)
+
+
+def pmc_summary(dirname):
+    """Average counter value per dispatch for every kernel in a --pmc csv run."""
+    import csv
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(_find(dirname, "counter_collection.csv"))):
+        acc[r["Kernel_Name"][:90]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: {"dispatches": len(v), "avg": sum(v) / len(v)} for c, v in d.items()}
+            for k, d in acc.items()}
+
+
+def bench_grouped_gemm(M, steps, warmup):
+    """The standalone FP8 grouped GEMM: 16 groups with Zipf(1.1) sizes summing to 8192
+    rows, each padded to 128; N=4096, K=7168; bf16 out.  A 512 MB write between timed
+    launches (outside the events) evicts the weights from the last-level cache."""
+    dev = torch.device("cuda:0")
+    sizes = synth.zipf_group_sizes(8192, 16, 1.1, seed=0)
+    N, K = 4096, 7168
+    padded = -(-sizes // 128) * 128
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    R = int(offsets[-1])
+    g = synth.gemm_inputs(sizes, N, K, seed=0, device=dev)
+    dest = np.concatenate([np.arange(offsets[i], offsets[i] + sizes[i]) for i in range(16)])
+    a = torch.zeros((R, K), dtype=torch.float32, device=dev)
+    a[torch.from_numpy(dest).to(dev)] = g["a"]
+    qa, sa = M.moe_quant_fp8(a)
+    qb, sb = M.moe_quant_weight_fp8(g["b"])
+    off = torch.from_numpy(offsets).to(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        M.grouped_gemm_fp8(qa, sa, qb, sb, off, R, N)
+    torch.cuda.synchronize()
+    tot = 0.0
+    for _ in range(steps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        M.grouped_gemm_fp8(qa, sa, qb, sb, off, R, N)
+        e1.record()
+        torch.cuda.synchronize()
+        tot += e0.elapsed_time(e1)
+    ms = tot / steps
+    flops = 2.0 * float(sizes.sum()) * N * K
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"metric": "FP8 grouped-GEMM TFLOPS on 1 MI355X (% roofline)", "value": round(tflops, 1),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+            "config": {"workload": "grouped_gemm_fp8: 16 Zipf(1.1) groups sum 8192 (padded to "
+                                   "128), N=4096, K=7168, bf16 out", "group_sizes": sizes.tolist()},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                         "traffic": None}}
 
 
 def stage_times(M, w, inp, weights, steps):
