@@ -19,7 +19,7 @@ from ._lib import (MOE_BF16, MOE_E4M3, MOE_EPI_PLAIN, MOE_EPI_SWIGLU, MOE_F32, M
 
 __all__ = [
     "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route",
-    "moe_route_from_logits", "moe_route_hash", "moe_dispatch", "moe_quant_fp8",
+    "moe_route_from_logits", "moe_route_hash", "moe_route_workspace_size", "moe_dispatch", "moe_quant_fp8",
     "moe_quant_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_w4a16",
     "grouped_gemm_f32", "moe_combine", "moe_layer_workspace_size", "moe_layer_fwd", "MoeError",
     "LayerDesc",
@@ -79,10 +79,16 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor, k: in
     logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    nws = _lib_().moe_route_workspace_size(T, d, E, _dt(x))
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     _lib.check(_lib_().moe_route(_ptr(x), _dt(x), _ptr(w_router), _ptr(bias), T, d, E, k,
                                  MOE_ROUTE_RENORM if renorm else 0, _ptr(logits), _ptr(idx),
-                                 _ptr(w), _stream(dev)), "moe_route")
+                                 _ptr(w), _ptr(ws), nws, _stream(dev)), "moe_route")
     return idx, w, logits
+
+
+def moe_route_workspace_size(T: int, d: int, E: int, dtype=torch.bfloat16) -> int:
+    return _lib_().moe_route_workspace_size(T, d, E, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
 
 
 def moe_route_from_logits(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,

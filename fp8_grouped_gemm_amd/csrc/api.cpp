@@ -142,14 +142,21 @@ int moe_route_from_logits(const float* logits, const float* bias, int T, int E, 
   if (st) return st;
   if (T == 0) return MOE_OK;
   if ((st = current_device(nullptr))) return st;
-  return hip_status(moe::launch_topk(logits, bias, T, E, k, flags & MOE_ROUTE_RENORM, topk_idx,
-                                     topk_w, S(stream)),
+  // with one partial plane the kernel only reads the logits
+  return hip_status(moe::launch_topk(const_cast<float*>(logits), nullptr, 1, bias, T, E, k,
+                                     flags & MOE_ROUTE_RENORM, topk_idx, topk_w, S(stream)),
                     "topk launch");
+}
+
+size_t moe_route_workspace_size(int T, int d, int E, moe_dtype x_dt) {
+  if (T <= 0 || E < 1 || d < 128 || x_dt != MOE_BF16 || d % 128) return 0;
+  const int n = moe::router_splits(T, d, E, true);
+  return n > 1 ? (size_t)n * T * E * sizeof(float) : 0;
 }
 
 int moe_route(const void* x, moe_dtype x_dt, const void* w_router, const float* bias, int T, int d,
               int E, int k, unsigned flags, float* logits, int32_t* topk_idx, float* topk_w,
-              void* stream) {
+              void* ws, size_t ws_bytes, void* stream) {
   REQUIRE(x && w_router, "moe_route: null pointer");
   REQUIRE(x_dt == MOE_BF16 || x_dt == MOE_F32, "moe_route: x_dt must be MOE_BF16 or MOE_F32");
   REQUIRE(d >= 1, "moe_route: d must be positive");
@@ -158,11 +165,16 @@ int moe_route(const void* x, moe_dtype x_dt, const void* w_router, const float* 
   if (st) return st;
   if (T == 0) return MOE_OK;
   if ((st = current_device(nullptr))) return st;
-  if ((st = hip_status(moe::launch_router(x, x_dt == MOE_BF16, w_router, logits, T, d, E, S(stream)),
+  const size_t need = moe_route_workspace_size(T, d, E, x_dt);
+  const int n_part = (need > 0 && ws && ws_bytes >= need)
+                         ? moe::router_splits(T, d, E, x_dt == MOE_BF16) : 1;
+  float* part = static_cast<float*>(ws);
+  if ((st = hip_status(moe::launch_router(x, x_dt == MOE_BF16, w_router, logits, T, d, E, part,
+                                          n_part, S(stream)),
                        "router launch")))
     return st;
-  return hip_status(moe::launch_topk(logits, bias, T, E, k, flags & MOE_ROUTE_RENORM, topk_idx,
-                                     topk_w, S(stream)),
+  return hip_status(moe::launch_topk(logits, part, n_part, bias, T, E, k,
+                                     flags & MOE_ROUTE_RENORM, topk_idx, topk_w, S(stream)),
                     "topk launch");
 }
 
@@ -304,7 +316,7 @@ int moe_combine(const void* o, moe_dtype o_dt, const int32_t* row_of_slot, const
 namespace {
 
 struct LayerWs {
-  size_t logits, idx, w, counts, offsets, ros, sor, qx, sx, h, sh, o, total;
+  size_t part, logits, idx, w, counts, offsets, ros, sor, qx, sx, h, sh, o, total;
 };
 
 int layer_check(const moe_layer_desc* d) {
@@ -335,6 +347,8 @@ LayerWs layer_ws(const moe_layer_desc* d) {
   const size_t R = moe_rows_bound(d->T, d->k, d->E, d->m_align);
   size_t p = 0;
   auto take = [&](size_t bytes) { size_t at = p; p = align_up(p + bytes); return at; };
+  L.part = take(d->route == MOE_ROUTE_SCORE && d->mode != MOE_MODE_FP32
+                    ? moe_route_workspace_size(d->T, d->d, d->E, MOE_BF16) : 0);
   L.logits = take(d->route == MOE_ROUTE_SCORE ? T * E * 4 : 0);
   L.idx = take(T * k * 4);
   L.w = take(T * k * 4);
@@ -402,8 +416,12 @@ int moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* w, const voi
   if ((st = hip_status((expr), what))) return st;
 
   if (d->route == MOE_ROUTE_SCORE) {
-    STEP(moe::launch_router(x, !f32, w->w_router, logits, T, D, E, s), "router launch");
-    STEP(moe::launch_topk(logits, w->bias, T, E, k, d->route_flags & MOE_ROUTE_RENORM, idx, gw, s),
+    const int n_part = f32 ? 1 : moe::router_splits(T, D, E, true);
+    float* part = reinterpret_cast<float*>(base + L.part);
+    STEP(moe::launch_router(x, !f32, w->w_router, logits, T, D, E, part, n_part, s),
+         "router launch");
+    STEP(moe::launch_topk(logits, part, n_part, w->bias, T, E, k,
+                          d->route_flags & MOE_ROUTE_RENORM, idx, gw, s),
          "topk launch");
   } else {
     STEP(moe::launch_hash_route(token_ids, T, E, idx, gw, s), "hash route launch");

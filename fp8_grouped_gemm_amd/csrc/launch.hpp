@@ -7,10 +7,13 @@
 
 namespace moe {
 
+// split-K planes the router uses for this shape (1 = no split, partials unused)
+int router_splits(int T, int d, int E, bool bf16);
 hipError_t launch_router(const void* x, bool bf16, const void* w, float* logits, int T, int d,
-                         int E, hipStream_t s);
-hipError_t launch_topk(const float* logits, const float* bias, int T, int E, int k, bool renorm,
-                       int32_t* idx, float* w, hipStream_t s);
+                         int E, float* part, int n_part, hipStream_t s);
+// n_part > 1: logits are the plane-order sums of part[n_part][T][E], written by this call
+hipError_t launch_topk(float* logits, const float* part, int n_part, const float* bias, int T,
+                       int E, int k, bool renorm, int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_hash_route(const int64_t* ids, int T, int E, int32_t* idx, float* w,
                              hipStream_t s);
 hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int m_align, int cap,

@@ -3,6 +3,8 @@
 //
 // The gate is one linear layer followed by softmax(W_g x + b) (MegaMoE walkthrough,
 // discosf.com sec. 2.2) computed in fp32 (DeepSeek-V4 lecture, tqpw.cn sec. 2.3).
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,12 +23,15 @@ constexpr int RT_LOADS = RT_BM * RT_CPR / 256;            // per thread per oper
 
 __global__ __launch_bounds__(256) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ logits,
-    int T, int d, int E) {
+    int T, int d, int E, int chunks_per_split) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][RT_BM * RT_ROWB];  // [A|B][row*256]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int m0 = blockIdx.x * RT_BM, n0 = blockIdx.y * RT_BN;
   const int wm = wid >> 1, wn = wid & 1;
-  const int nchunk = d / RT_BK;
+  // split-K: this workgroup sums K chunks [c0, c0 + nchunk) into partial plane blockIdx.z
+  const int c0 = blockIdx.z * chunks_per_split;
+  const int nchunk = min(chunks_per_split, d / RT_BK - c0);
+  logits += (size_t)blockIdx.z * T * E;
 
   const uint8_t* a_ptr[RT_LOADS];
   const uint8_t* b_ptr[RT_LOADS];
@@ -36,8 +41,8 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     int c = tid + i * 256;
     int row = c / RT_CPR, piece = c % RT_CPR;
     int ar = min(m0 + row, T - 1), br = min(n0 + row, E - 1);
-    a_ptr[i] = reinterpret_cast<const uint8_t*>(x + (size_t)ar * d) + piece * 16;
-    b_ptr[i] = reinterpret_cast<const uint8_t*>(w + (size_t)br * d) + piece * 16;
+    a_ptr[i] = reinterpret_cast<const uint8_t*>(x + (size_t)ar * d + (size_t)c0 * RT_BK) + piece * 16;
+    b_ptr[i] = reinterpret_cast<const uint8_t*>(w + (size_t)br * d + (size_t)c0 * RT_BK) + piece * 16;
     lds_off[i] = row * RT_ROWB + ((piece ^ (row & 15)) * 16);
   }
   v4i ra[2][RT_LOADS], rb[2][RT_LOADS];
@@ -117,8 +122,11 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict
 // One wave per token.  Keys key_e = fl32(logit_e + b_e) live KPL per lane (expert
 // e = lane + 64*i).  k rounds of a wave arg-max pick the largest key, the lower
 // expert index winning ties; the softmax over all E keys is taken in fp32.
+// With n_part > 1 the logits arrive as split-K partial planes part[n_part][T][E]; they
+// are summed here in plane order (deterministic) and the sums written to logits.
 template <int KPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void topk_kernel(float* __restrict__ logits,
+                                                   const float* __restrict__ part, int n_part,
                                                    const float* __restrict__ bias, int T,
                                                    int E, int k, int renorm,
                                                    int32_t* __restrict__ idx,
@@ -126,14 +134,25 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
+  float* row = logits + (size_t)t * E;
   float key[KPL];
   bool live[KPL];
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     int e = lane + 64 * i;
     live[i] = e < E;
-    key[i] = live[i] ? row[e] + (bias ? bias[e] : 0.0f) : -INFINITY;
+    float l = 0.f;
+    if (live[i]) {
+      if (n_part > 1) {
+        const float* pp = part + (size_t)t * E + e;
+        l = pp[0];
+        for (int s = 1; s < n_part; ++s) l += pp[(size_t)s * T * E];
+        row[e] = l;
+      } else {
+        l = row[e];
+      }
+    }
+    key[i] = live[i] ? l + (bias ? bias[e] : 0.0f) : -INFINITY;
   }
   // softmax denominator over every expert
   float m = -INFINITY;
@@ -187,13 +206,24 @@ __global__ void hash_route_kernel(const int64_t* __restrict__ ids, int T, int E,
 }
 
 // ------------------------------------------------------------------ launchers
+int router_splits(int T, int d, int E, bool bf16) {
+  if (!bf16) return 1;
+  const long tiles = (long)((T + RT_BM - 1) / RT_BM) * ((E + RT_BN - 1) / RT_BN);
+  const int chunks = d / RT_BK;
+  int want = (int)std::min<long>(std::max<long>(1, (1024 + tiles - 1) / tiles), chunks);
+  const int cps = (chunks + want - 1) / want;
+  return (chunks + cps - 1) / cps;
+}
+
 hipError_t launch_router(const void* x, bool bf16, const void* w, float* logits, int T, int d,
-                         int E, hipStream_t s) {
+                         int E, float* part, int n_part, hipStream_t s) {
   if (bf16) {
-    dim3 grid((T + RT_BM - 1) / RT_BM, (E + RT_BN - 1) / RT_BN);
+    const int chunks = d / RT_BK;
+    const int cps = (chunks + n_part - 1) / n_part;
+    dim3 grid((T + RT_BM - 1) / RT_BM, (E + RT_BN - 1) / RT_BN, n_part);
     hipLaunchKernelGGL(router_bf16_kernel, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), logits,
-                       T, d, E);
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                       n_part > 1 ? part : logits, T, d, E, cps);
   } else {
     int n = T * E;
     hipLaunchKernelGGL(router_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
@@ -203,20 +233,19 @@ hipError_t launch_router(const void* x, bool bf16, const void* w, float* logits,
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, const float* bias, int T, int E, int k, bool renorm,
-                       int32_t* idx, float* w, hipStream_t s) {
+hipError_t launch_topk(float* logits, const float* part, int n_part, const float* bias, int T,
+                       int E, int k, bool renorm, int32_t* idx, float* w, hipStream_t s) {
   dim3 grid((T + 3) / 4), block(256);
   int r = renorm ? 1 : 0;
-  if (E <= 64)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, bias, T, E, k, r, idx, w);
-  else if (E <= 128)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, bias, T, E, k, r, idx, w);
-  else if (E <= 256)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, bias, T, E, k, r, idx, w);
-  else if (E <= 512)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, bias, T, E, k, r, idx, w);
-  else
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, bias, T, E, k, r, idx, w);
+#define MOE_TOPK(KPL) \
+  hipLaunchKernelGGL(topk_kernel<KPL>, grid, block, 0, s, logits, part, n_part, bias, T, E, k, \
+                     r, idx, w)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 256) MOE_TOPK(4);
+  else if (E <= 512) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 

@@ -85,21 +85,28 @@ int moe_capacity(int T, int k, int E, double factor);
 size_t moe_rows_bound(int T, int k, int E, int m_align);
 
 /* Router: logits = x . w_router^T, then the biased softmax top-k of
- * moe_route_from_logits.  s_i = softmax(W_g x + b_i) (discosf.com sec. 2.2); the
- * softmax runs in fp32 (tqpw.cn sec. 2.3).
+ * moe_route_from_logits.  s_i = softmax(W_g x + b_i) (MegaMoE walkthrough, discosf.com,
+ * sec. 2.2); the softmax runs in fp32 (DeepSeek-V4 lecture, tqpw.cn, sec. 2.3).
  *   x [T, d] and w_router [E, d] of dtype x_dt (MOE_BF16 or MOE_F32, both the same);
- *   bias [E] fp32; logits [T, E] fp32 output (required: it is the staging buffer);
- *   topk_idx [T, k] int32 and topk_w [T, k] fp32 outputs.
- *   1 <= k <= E <= 1024; d a multiple of 128 for MOE_BF16. */
+ *   bias [E] fp32; logits [T, E] fp32 output (always written);
+ *   topk_idx [T, k] int32 and topk_w [T, k] fp32 outputs;
+ *   ws / ws_bytes: optional device workspace for split-K partial logits; with at least
+ *   moe_route_workspace_size() bytes the logit product is split along d over more
+ *   workgroups (summed in a fixed order, so results do not depend on it); NULL or
+ *   smaller runs unsplit.
+ *   1 <= k <= min(E, 64), E <= 1024; d a multiple of 128 for MOE_BF16. */
 int moe_route(const void *x, moe_dtype x_dt, const void *w_router, const float *bias,
               int T, int d, int E, int k, unsigned flags, float *logits,
-              int32_t *topk_idx, float *topk_w, void *stream);
+              int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes moe_route uses to split the logit product (0: it never splits). */
+size_t moe_route_workspace_size(int T, int d, int E, moe_dtype x_dt);
 
 /* Top-k of fp32 logits [T, E] with per-expert bias [E] (bias may be NULL = 0).
  * key_e = fl32(logit_e + b_e); the k largest keys are chosen, largest first, equal
  * keys to the lower expert index; topk_w[t, j] = softmax over all E keys at
  * topk_idx[t, j] (or, with MOE_ROUTE_RENORM, divided by the sum of the k chosen).
- * Logits must be finite.  1 <= k <= E <= 1024. */
+ * Logits must be finite.  1 <= k <= min(E, 64), E <= 1024. */
 int moe_route_from_logits(const float *logits, const float *bias, int T, int E, int k,
                           unsigned flags, int32_t *topk_idx, float *topk_w, void *stream);
 

@@ -23,7 +23,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = _lib.load()
     declared = _declared()
-    assert len(declared) == 17, declared
+    assert len(declared) == 18, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -58,10 +58,14 @@ def test_route_rejects_bad_args():
     _err(lib.moe_route_from_logits(FAKE, None, 4, 8, 9, 0, FAKE, FAKE, S), "k must")
     _err(lib.moe_route_from_logits(FAKE, None, 4, 2000, 2, 0, FAKE, FAKE, S), "E must")
     _err(lib.moe_route_from_logits(FAKE, None, 4, 8, 2, 4, FAKE, FAKE, S), "flags")
-    _err(lib.moe_route(FAKE, _lib.MOE_E4M3, FAKE, FAKE, 4, 256, 8, 2, 0, FAKE, FAKE, FAKE, S),
-         "x_dt")
-    _err(lib.moe_route(FAKE, _lib.MOE_BF16, FAKE, FAKE, 4, 200, 8, 2, 0, FAKE, FAKE, FAKE, S),
-         "128")
+    _err(lib.moe_route(FAKE, _lib.MOE_E4M3, FAKE, FAKE, 4, 256, 8, 2, 0, FAKE, FAKE, FAKE,
+                       None, 0, S), "x_dt")
+    _err(lib.moe_route(FAKE, _lib.MOE_BF16, FAKE, FAKE, 4, 200, 8, 2, 0, FAKE, FAKE, FAKE,
+                       None, 0, S), "128")
+    # split-K partial planes: T*E floats per plane, none for fp32 or tiny shapes
+    n = lib.moe_route_workspace_size(128, 7168, 256, _lib.MOE_BF16)
+    assert n > 0 and n % (128 * 256 * 4) == 0
+    assert lib.moe_route_workspace_size(128, 7168, 256, _lib.MOE_F32) == 0
     _err(lib.moe_route_hash(None, 4, 8, FAKE, FAKE, S), "null")
 
 
