@@ -272,8 +272,7 @@ int grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_rows, int a_row_div, 
   if (st) return st;
   REQUIRE(s7, "grouped_gemm_w4a16: null scale pointer");
   REQUIRE(K % 128 == 0, "grouped_gemm_w4a16: K must be a multiple of 128");
-  REQUIRE(N % (epilogue == MOE_EPI_SWIGLU ? 64 : 128) == 0,
-          "grouped_gemm_w4a16: N must be a multiple of 64 (SwiGLU) or 128");
+  REQUIRE(N % 128 == 0, "grouped_gemm_w4a16: N must be a multiple of 128");
   REQUIRE(a_row_div >= 1, "grouped_gemm_w4a16: a_row_div must be >= 1");
   if (R_cap == 0) return MOE_OK;
   int cus = 0;

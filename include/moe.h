@@ -173,7 +173,7 @@ int grouped_gemm_fp8(const uint8_t *A, const float *sA, const int32_t *a_rows, i
 /* Grouped GEMM with int4 weights and bf16 activations: B codes [G, Nb, K/2] and
  * s7 [G, Nb, K/128] are dequantised in-kernel to bf16(fl32(q * s7)) and multiplied with
  * A [*, K] bf16 in fp32.  Row gather and epilogues as grouped_gemm_fp8; output C
- * [R_cap, N] bf16.  N multiple of 64, K multiple of 128. */
+ * [R_cap, N] bf16.  N and K multiples of 128. */
 int grouped_gemm_w4a16(const uint16_t *A, const int32_t *a_rows, int a_row_div,
                        const uint8_t *B, const float *s7, const int32_t *offsets, int G,
                        int R_cap, int N, int K, int epilogue, uint16_t *C, void *stream);

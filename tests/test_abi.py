@@ -96,7 +96,7 @@ def test_gemm_and_combine_reject_bad_args():
     _err(lib.grouped_gemm_fp8(FAKE, None, None, 1, FAKE, FAKE, FAKE, 2, 128, 128, 128, 0,
                               _lib.MOE_BF16, FAKE, None, S), "scale")
     _err(lib.grouped_gemm_w4a16(FAKE, None, 1, FAKE, FAKE, FAKE, 2, 64, 96, 128, 1, FAKE, S),
-         "multiple of 64")
+         "multiple of 128")
     _err(lib.grouped_gemm_f32(FAKE, None, 1, FAKE, FAKE, 2, 64, 24, 128, 0, FAKE, S),
          "multiple of 16")
     _err(lib.moe_combine(FAKE, _lib.MOE_BF16, FAKE, FAKE, 4, 2, 12, FAKE, _lib.MOE_BF16, S),
