@@ -27,10 +27,14 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in VGPRs: the promotion FMAs read them without accvgpr moves
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"),
 ]
+# per-source additions
+FILE_FLAGS = {
+    # FP8 GEMM: MFMA results in VGPRs, so the per-block promotion FMAs read them without
+    # accvgpr moves (the W4A16 GEMM keeps its accumulators in AGPRs, the default)
+    "gemm_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def sources():
@@ -40,7 +44,8 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-x", "hip", "-c", src,
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -15,6 +15,8 @@
 // wave).  Gathered activation rows, packed codes
 // and scales arrive by direct global->LDS DMA in three stages, in the same persistent,
 // XCD-aware tile order as the FP8 kernel.
+#include <type_traits>
+
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
@@ -34,18 +36,52 @@ struct W4Args {
   uint16_t* C;
 };
 
-// 8 int4 codes (two's complement nibbles, element 2b low / 2b+1 high nibble of byte b)
-// -> 8 bf16 values bf16(fl32(q * s)), in k order; off = -8 s.
-__device__ __forceinline__ v8bf expand8(uint32_t w, float s, float off) {
-  const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;          // q + 8 of even k
-  const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // q + 8 of odd k
-  v8bf r;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    r[2 * b] = (__bf16)fmaf((float)((lo >> (8 * b)) & 0xFFu), s, off);
-    r[2 * b + 1] = (__bf16)fmaf((float)((hi >> (8 * b)) & 0xFFu), s, off);
-  }
-  return r;
+// Codes of one row and 128-wide K block, as stored: 64 little-endian 32-bit words, word
+// p holding k = 8p .. 8p+7 -- byte b carries k = 8p+b in its low nibble and k = 8p+4+b
+// in its high nibble, each nibble sign (bit 3) and magnitude (bits 0-2, at most 7).
+//
+// Expansion by table: bf16(fl32(m * s)) for the eight magnitudes m is built once per row
+// and K block and split into its low bytes (l0: m 0-3, l1: m 4-7) and high bytes (h0,
+// h1).  A byte permute then looks up four codes at once; the sign goes into bit 15
+// (bf16 of fl32(-m s) is the negated bf16 of fl32(m s)).
+struct Tab {
+  uint32_t l0, l1, h0, h1;
+};
+
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  const v2bf v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ Tab make_tab(float s) {
+  // entries m = 2i (low half) and 2i + 1 (high half); fl32(m * s) by one rounding
+  const uint32_t p0 = bf16x2(0.0f, s);
+  const uint32_t p1 = bf16x2(2.0f * s, 3.0f * s);
+  const uint32_t p2 = bf16x2(4.0f * s, 5.0f * s);
+  const uint32_t p3 = bf16x2(6.0f * s, 7.0f * s);
+  // perm(hi, lo, sel): result byte i = byte sel_i of the 8 bytes lo (0-3), hi (4-7)
+  Tab t;
+  t.l0 = __builtin_amdgcn_perm(p1, p0, 0x06040200u);
+  t.l1 = __builtin_amdgcn_perm(p3, p2, 0x06040200u);
+  t.h0 = __builtin_amdgcn_perm(p1, p0, 0x07050301u);
+  t.h1 = __builtin_amdgcn_perm(p3, p2, 0x07050301u);
+  return t;
+}
+
+// one code word -> the 8 bf16 weights of k = 8p .. 8p+7, in k order
+__device__ __forceinline__ v8bf expand8(uint32_t w, const Tab& t) {
+  const uint32_t m03 = w & 0x07070707u;
+  const uint32_t m47 = (w >> 4) & 0x07070707u;
+  const uint32_t l03 = __builtin_amdgcn_perm(t.l1, t.l0, m03);
+  const uint32_t l47 = __builtin_amdgcn_perm(t.l1, t.l0, m47);
+  const uint32_t h03 = __builtin_amdgcn_perm(t.h1, t.h0, m03) | ((w << 4) & 0x80808080u);
+  const uint32_t h47 = __builtin_amdgcn_perm(t.h1, t.h0, m47) | (w & 0x80808080u);
+  const v4i r = {(int)__builtin_amdgcn_perm(h03, l03, 0x05010400u),
+                 (int)__builtin_amdgcn_perm(h03, l03, 0x07030602u),
+                 (int)__builtin_amdgcn_perm(h47, l47, 0x05010400u),
+                 (int)__builtin_amdgcn_perm(h47, l47, 0x07030602u)};
+  return __builtin_bit_cast(v8bf, r);
 }
 }  // namespace
 
@@ -55,7 +91,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
   constexpr int BNO = SWIGLU ? 128 : 256;           // output columns per tile
   constexpr int NS = 3;                             // DMA stages
   constexpr int ROWB = 256;                         // A bytes per row per K block
-  constexpr int TM = 8, TN = 4;                     // per wave: 128 rows x 64 weight rows
+  constexpr int TN = 2;                             // per wave: 2 x 32 weight rows
   constexpr int A_IN = BM * ROWB / 1024 / 4;        // A DMA instructions per wave: 8
   constexpr int B_IN = BNB * 64 / 1024 / 4;         // code DMA instructions per wave: 4
   constexpr int PER_MAX = A_IN + B_IN + 1;          // + the scales
@@ -71,7 +107,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q4 = lane >> 4, l16 = lane & 15;
+  const int hf = lane >> 5, l32 = lane & 31;       // 32x32x16 MFMA operand: row l32, k half hf
   const int G = args.G, K = args.K, N = args.N, KB = K / 128;
   const int NBtot = SWIGLU ? 2 * N : N;
   const int tiles_n = (N + BNO - 1) / BNO;
@@ -90,35 +126,20 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
     return s < 32 ? n0 + 32 * w + s : N + n0 + 32 * w + s - 32;
   };
 
-  for (int t = v; t < total; t += P) {
-    const int g = find_group(tm, G, t, tiles_n);
-    const int mt = tm.start[g + 1] - tm.start[g];
-    const int local = t - tm.start[g] * tiles_n;
-    const int ni = local / mt, mi = local % mt;
-    const int row0 = tm.off[g] + mi * BM, row_end = tm.off[g + 1];
-    const int n_valid = min(row_end - row0, BM);   // >= 1
-    const int tmv = (n_valid + 15) >> 4;           // 16-row blocks with a real row
-    const int n0 = ni * BNO;
+  // one tile whose real rows lie in its first TM 32-row blocks
+  auto run_tile = [&](auto TMC, int g, int row0, int n_valid, int n0) {
+    constexpr int TM = decltype(TMC)::value;
     const int ncols = min(BNO, N - n0);            // plain N % 256 == 128: last tile half
-    const bool wactive = SWIGLU || wid * 64 < ncols;
-    if (tid < BM) {
-      int lr = min(row0 + tid, row_end - 1), src = lr;
-      if (args.a_rows) {
-        int sr = args.a_rows[lr];
-        src = sr < 0 ? 0 : sr / args.a_row_div;
-      }
-      row_src[tid] = src;
-    }
-    __syncthreads();
+    const bool wactive = SWIGLU || wid * 64 < ncols;  // else: repeated rows, not stored
 
     // A: an instruction fills 4 rows of 256 B; lane L lands at row L/16, slot L%16 and
     // fetches 16-byte piece (L%16) ^ (row%16), the XOR swizzle read back below.
     const uint8_t* a_src[A_IN];
 #pragma unroll
     for (int i = 0; i < A_IN; ++i) {
-      const int row = (wid * A_IN + i) * 4 + q4;
+      const int row = (wid * A_IN + i) * 4 + (lane >> 4);
       a_src[i] = reinterpret_cast<const uint8_t*>(args.A + (size_t)row_src[row] * K) +
-                 ((l16 ^ (row & 15)) << 4);
+                 (((lane & 15) ^ (row & 15)) << 4);
     }
     const int a_cnt = min(max((n_valid - wid * A_IN * 4 + 3) / 4, 0), A_IN);
     const int per = a_cnt + B_IN + 1;
@@ -143,11 +164,13 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
       dma4(s_src + kb, m_s + so);
     };
 
-    v4f acc[TM][TN];
+    v16f acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // K loop: buffers hold blocks kb, kb+1, kb+2; one barrier per block publishes block
     // kb and certifies that every wave is done with block kb-1, whose buffer is refilled.
@@ -159,34 +182,59 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
       __builtin_amdgcn_s_barrier();
       if (kb + 2 < KB) issue(st == 0 ? 2 : st - 1, kb + 2);
       const uint8_t* L = lds[st];
-      // this lane's codes: weight row 64 * wave + 16 j + l16, k = 32 q4 .. 32 q4 + 31
-      v4i raw[TN];
-      float sc[TN], so[TN];
+      // MFMA step kk takes k = 64 hf + 8 kk + e from lane (l32, hf): code word 8 hf + kk
+      // of the weight row and 16-byte piece 8 hf + kk of the A row, one k order for both.
+      v4i raw[TN][2];
+      Tab tab[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int r = wid * 64 + j * 16 + l16;
-        raw[j] = *reinterpret_cast<const v4i*>(L + BR_OFF + r * 64 + q4 * 16);
-        sc[j] = reinterpret_cast<const float*>(L + SC_OFF)[r];
-        so[j] = -8.0f * sc[j];
+        const int r = wid * 64 + j * 32 + l32;
+        const uint8_t* src = L + BR_OFF + r * 64 + hf * 32;
+        raw[j][0] = *reinterpret_cast<const v4i*>(src);
+        raw[j][1] = *reinterpret_cast<const v4i*>(src + 16);
+        tab[j] = make_tab(reinterpret_cast<const float*>(L + SC_OFF)[r]);
       }
-      // fragment ks holds k = 8 * (4 q4 + ks) + e, for A and B alike
+      auto expand_step = [&](int kk, v8bf* bf) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        v8bf bf[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = expand8((uint32_t)raw[j][ks], sc[j], so[j]);
-        const int piece = 4 * q4 + ks;
+        for (int j = 0; j < TN; ++j) bf[j] = expand8((uint32_t)raw[j][kk >> 2][kk & 3], tab[j]);
+      };
+      auto read_step = [&](int kk, v8bf* af) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          if (wactive && i < tmv) {
-            const int row = i * 16 + l16;
-            const v8bf af =
-                *reinterpret_cast<const v8bf*>(L + row * ROWB + ((piece ^ (row & 15)) << 4));
+          const int row = i * 32 + l32;
+          af[i] = *reinterpret_cast<const v8bf*>(L + row * ROWB +
+                                                 (((8 * hf + kk) ^ (row & 15)) << 4));
+        }
+      };
+      // software pipeline over the 8 steps: while the TM x TN MFMAs of step kk run, the
+      // wave reads the A fragments and expands the weights of step kk + 1
+      v8bf af[2][TM], bf[2][TN];
+      read_step(0, af[0]);
+      expand_step(0, bf[0]);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+      for (int kk = 0; kk < 8; ++kk) {
+        const int c = kk & 1;
+        if (kk + 1 < 8) {
+          read_step(kk + 1, af[c ^ 1]);
+          expand_step(kk + 1, bf[c ^ 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j],
+                                                                0, 0, 0);
+        // issue order: each MFMA followed by a share of the next step's LDS reads and
+        // expansion (left alone, the scheduler sinks them to their uses)
+        if (kk + 1 < 8) {
+#pragma unroll
+          for (int m = 0; m < TM * TN; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+            if (m < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 28 / (TM * TN) + 1, 0);  // VALU
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       st = st == NS - 1 ? 0 : st + 1;
     }
@@ -195,28 +243,25 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
     __syncthreads();
     uint8_t* ot = &lds[0][0];
     constexpr int OB = BNO * 2;
+    // accumulator element r of lane (l32, hf): row 8 (r / 4) + 4 hf + r % 4, column l32
+    if (wactive) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (wactive && i < tmv) {
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int trow = i * 16 + q4 * 4 + r;
+        for (int r = 0; r < 16; ++r) {
+          const int trow = i * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
           if (SWIGLU) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const int tcol = wid * 32 + j * 16 + l16;
-              const float hv = silu(acc[i][j][r]) * acc[i][j + 2][r];
-              *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(hv);
-            }
+            const int tcol = wid * 32 + l32;
+            const float hv = silu(acc[i][0][r]) * acc[i][1][r];
+            *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(hv);
           } else {
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-              const int tcol = wid * 64 + j * 16 + l16;
+              const int tcol = wid * 64 + j * 32 + l32;
               *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(acc[i][j][r]);
             }
           }
         }
-      }
     }
     __syncthreads();
     const int CPR = ncols / 8;                     // 16-byte chunks per output row
@@ -227,6 +272,30 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
           *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
     }
     __syncthreads();
+  };
+
+  for (int t = v; t < total; t += P) {
+    const int g = find_group(tm, G, t, tiles_n);
+    const int mt = tm.start[g + 1] - tm.start[g];
+    const int local = t - tm.start[g] * tiles_n;
+    const int ni = local / mt, mi = local % mt;
+    const int row0 = tm.off[g] + mi * BM, row_end = tm.off[g + 1];
+    const int n_valid = min(row_end - row0, BM);   // >= 1
+    if (tid < BM) {
+      int lr = min(row0 + tid, row_end - 1), src = lr;
+      if (args.a_rows) {
+        int sr = args.a_rows[lr];
+        src = sr < 0 ? 0 : sr / args.a_row_div;
+      }
+      row_src[tid] = src;
+    }
+    __syncthreads();
+    if (n_valid <= 32)
+      run_tile(std::integral_constant<int, 1>{}, g, row0, n_valid, ni * BNO);
+    else if (n_valid <= 64)
+      run_tile(std::integral_constant<int, 2>{}, g, row0, n_valid, ni * BNO);
+    else
+      run_tile(std::integral_constant<int, 4>{}, g, row0, n_valid, ni * BNO);
   }
 }
 

@@ -119,13 +119,16 @@ __global__ __launch_bounds__(256) void quant_weight_int4_kernel(const float* __r
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = group_max<16>(amax);
   if (amax == 0.f) amax = 1.f;
+  // one 32-bit word per 8 codes: byte b holds code b (low nibble) and code 4 + b (high),
+  // each nibble sign (bit 3) and magnitude
   uint32_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float t = v[i] / amax;
     t = t * 7.0f;
-    int qi = (int)rintf(t);
-    packed |= ((uint32_t)qi & 0xFu) << (4 * i);
+    const int qi = (int)rintf(t);
+    const uint32_t nib = qi < 0 ? (8u | (uint32_t)(-qi)) : (uint32_t)qi;
+    packed |= nib << (8 * (i & 3) + 4 * (i >> 2));
   }
   *reinterpret_cast<uint32_t*>(q + row * (K / 2) + kb * 64 + li * 4) = packed;
   if (li == 0) s7[row * KB + kb] = amax / 7.0f;

@@ -51,7 +51,8 @@ typedef enum {
   MOE_F32 = 0,   /* IEEE fp32 */
   MOE_BF16 = 1,  /* bfloat16 stored as uint16 */
   MOE_E4M3 = 2,  /* OCP e4m3 ("fn": max 448, no infinities) stored as uint8 */
-  MOE_INT4 = 3   /* signed 4-bit codes in [-7, 7], two per byte, low nibble first */
+  MOE_INT4 = 3   /* signed 4-bit codes in [-7, 7], sign-magnitude nibbles, two per byte:
+                    byte 4p+b holds code 8p+b (low nibble) and 8p+4+b (high nibble) */
 } moe_dtype;
 
 /* moe_route flags */
@@ -147,8 +148,8 @@ int moe_quant_weight_fp8(const float *w, int G, int N, int K, uint8_t *q, float 
 
 /* Block-wise int4 weights with 1x128 per-channel blocks (tqpw.cn sec. 3.1): for each
  * row n and 128-wide block, scale = max|w| (1 if 0), q = rne(fl32(fl32(w/scale)*7))
- * in [-7,7], s7 = fl32(scale/7).  w [G, N, K] fp32 -> q [G, N, K/2] packed (element
- * 2j in the low nibble), s7 [G, N, K/128] fp32.  K a multiple of 128. */
+ * in [-7,7], s7 = fl32(scale/7).  w [G, N, K] fp32 -> q [G, N, K/2] packed as
+ * MOE_INT4 describes, s7 [G, N, K/128] fp32.  K a multiple of 128. */
 int moe_quant_weight_int4(const float *w, int G, int N, int K, uint8_t *q, float *s7,
                           void *stream);
 

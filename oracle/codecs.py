@@ -188,8 +188,19 @@ def int4_dequant(q, s7) -> np.ndarray:
 
 
 def int4_pack(q) -> np.ndarray:
-    """Pack int4 codes two per byte along K: element 2j in the low nibble, 2j+1 high."""
+    """Pack int4 codes [..., K] into bytes [..., K/2] (a storage layout of this library).
+
+    Every 8 consecutive codes k = 8p .. 8p+7 fill the 4 bytes 4p .. 4p+3: byte 4p+b holds
+    code 8p+b in its low nibble and code 8p+4+b in its high nibble.  A nibble is sign
+    (bit 3, set for negative codes) and magnitude (bits 0-2); codes lie in [-7, 7].
+    """
     q = np.asarray(q, dtype=np.int8)
-    lo = (q[..., 0::2].astype(np.int16) & 0xF)
-    hi = (q[..., 1::2].astype(np.int16) & 0xF)
-    return (lo | (hi << 4)).astype(np.uint8)
+    K = q.shape[-1]
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    if q.size and (q.min() < -7 or q.max() > 7):
+        raise ValueError("int4 codes must lie in [-7, 7]")
+    mag = np.abs(q.astype(np.int16))
+    nib = np.where(q < 0, 8 | mag, mag).reshape(*q.shape[:-1], K // 8, 8)
+    packed = nib[..., :4] | (nib[..., 4:] << 4)
+    return packed.reshape(*q.shape[:-1], K // 2).astype(np.uint8)

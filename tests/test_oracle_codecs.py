@@ -139,12 +139,24 @@ def test_int4_block_rules(golden):
     assert np.all(err <= scale / 14 + np.abs(w) * 2.0 ** -7 + 1e-7)
     packed = C.int4_pack(q)
     assert packed.shape == (2, 5, 128)
-    lo = (packed & 0xF).astype(np.int8)
-    lo = np.where(lo > 7, lo - 16, lo)
-    hi = (packed >> 4).astype(np.int8)
-    hi = np.where(hi > 7, hi - 16, hi)
-    np.testing.assert_array_equal(lo, q[..., 0::2])
-    np.testing.assert_array_equal(hi, q[..., 1::2])
+    # unpack byte by byte with the layout's rule, independently of the packer
+    flat = packed.reshape(-1, 128)
+    ref = q.reshape(-1, 256)
+    for row in range(flat.shape[0]):
+        for byte in range(128):
+            p, b = divmod(byte, 4)
+            v = int(flat[row, byte])
+            for nib, k in ((v & 0xF, 8 * p + b), (v >> 4, 8 * p + 4 + b)):
+                val = -(nib & 7) if nib & 8 else nib & 7
+                assert val == ref[row, k]
+
+
+def test_int4_pack_layout_example():
+    # codes 1, -2, 3, -4, 5, -6, 7, 0 -> nibbles 1, A, 3, C, 5, E, 7, 0 -> bytes 51 EA 73 0C
+    q = np.array([[1, -2, 3, -4, 5, -6, 7, 0]], np.int8)
+    assert C.int4_pack(q).tolist() == [[0x51, 0xEA, 0x73, 0x0C]]
+    with pytest.raises(ValueError):
+        C.int4_pack(np.full((1, 8), -8, np.int8))
 
 
 def test_fp4_bytes_example(golden):
