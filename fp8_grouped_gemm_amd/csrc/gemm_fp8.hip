@@ -14,9 +14,9 @@
 //   * v_mfma_f32_16x16x128_f8f6f4: one instruction covers one 16x16 output tile over
 //     exactly one 128-deep scale block, so promotion is one fp32 FMA per output per
 //     block: acc += (sA*sB) * mfma(a, b, 0).
-//   * 256 threads = 4 wave64s over a BM x BNB tile (BNB rows of B).  Prefill tiles are
-//     128 x 256 with 64 x 128 per wave, so one weight byte brought into LDS feeds 128
-//     token rows and every fragment read from LDS feeds 4 or 8 MFMAs.  A SwiGLU tile
+//   * 512 threads = 8 wave64s (two per SIMD) over a BM x BNB tile (BNB rows of B).
+//     Prefill tiles are 128 x 256 with 64 x 64 per wave, so one weight byte brought
+//     into LDS feeds 128 token rows and every fragment read from LDS feeds 4 MFMAs.  A SwiGLU tile
 //     loads 128 gate rows and 128 up rows of B so the 1x128 requant block is complete
 //     inside one workgroup.
 //   * Operands reach LDS by direct global->LDS DMA into 3 buffers (two K blocks in
@@ -53,27 +53,29 @@ struct GemmArgs {
 }  // namespace
 
 // Two tile classes share one persistent tile list: groups with at most BMS rows are
-// cut into BMS-row tiles worked by 4 waves side by side (all SIMDs busy, the weight
-// stream dominates), larger groups into 128-row tiles worked by 2 x 2 waves (a weight
+// cut into BMS-row tiles worked by 8 waves side by side (all SIMDs busy, the weight
+// stream dominates), larger groups into 128-row tiles worked by 2 x 4 waves (a weight
 // byte in LDS feeds 128 rows).  B tile: BNB rows (SWIGLU: BNB/2 gate + BNB/2 up rows ->
-// BNB/2 output columns; plain: BNB output columns).
+// BNB/2 output columns; plain: BNB output columns).  Eight waves, two per SIMD, so that
+// one wave's MFMAs cover the other's LDS reads and promotion arithmetic.
 template <int BMS, int BNB, bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
+__global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
+  constexpr int NT = 512, NW = 8;
   constexpr int NS = 3;
   constexpr int BMB = 128;                         // rows of a big-group tile
   constexpr int BN_OUT = SWIGLU ? BNB / 2 : BNB;   // output columns per tile
-  constexpr int B_IN = BNB / 32;                   // B DMA instructions per wave
-  constexpr int A_IN_MAX = BMB / 32;
+  constexpr int B_IN = BNB / 8 / NW;               // B DMA instructions per wave (8 rows each)
+  constexpr int A_IN_MAX = BMB / 8 / NW;           // A DMA instructions per wave, at most
   constexpr int PER_MAX = A_IN_MAX + B_IN + 1;     // + one scale load
   constexpr int A_BYTES = BMB * 128, B_BYTES = BNB * 128;
   constexpr int SC_OFF = A_BYTES + B_BYTES;        // 4 x 256 B of scale slots
   constexpr int STAGE = SC_OFF + 1024;
   static_assert(!SWIGLU || BN_OUT == 128, "1x128 requant block");
-  static_assert(PER_MAX < 16, "vmcnt encoding");
+  static_assert(B_IN >= 1 && A_IN_MAX >= 1 && PER_MAX < 16, "DMA split");
 
   __shared__ TileMap tm;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS][STAGE];
-  __shared__ float red[SWIGLU ? 4 : 1][SWIGLU ? BMB : 1];
+  __shared__ float red[SWIGLU ? 512 : 1];          // SwiGLU row maxima [wn][row]
   __shared__ int row_src[128];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -81,27 +83,30 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
   const int G = args.G, K = args.K, N = args.N, KB = K / 128;
   const int tiles_n = N / BN_OUT;
 
-  build_tile_map<BMS, BMB>(tm, args.offsets, G);
+  build_tile_map<BMS, BMB, NT>(tm, args.offsets, G);
   const int total = tm.start[G] * tiles_n;
   const int P = gridDim.x;
   const int b = blockIdx.x;
   const int v = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
   const uint32_t lds0 = lds_addr(&lds[0][0]);
-  const int lr8 = lane >> 3, slot = lane & 7, piece = slot ^ lr8;
+  const int lr8 = lane >> 3, slot = lane & 7;
+  // 16-byte piece p of row r sits in slot p ^ swz(r) of the row's 128 LDS bytes; pairs
+  // of rows share a 256-byte bank line, so the key changes every second row
+  auto swz = [](int r) { return (r >> 1) & 7; };
   const int gsel = 2 * (lane >> 4);
 
   // one tile of class BM (WM waves along M)
   auto run_tile = [&](auto BMC, int g, int row0, int row_end, int n0) {
     constexpr int BM = decltype(BMC)::value;
     constexpr int WM = BM == BMB ? 2 : 1;
-    constexpr int WN = 4 / WM;
+    constexpr int WN = NW / WM;
     constexpr int WTM = BM / WM;                   // rows per wave
     constexpr int TM = WTM / 16;                   // 16-row MFMA tiles per wave
     constexpr int WTN = BNB / WN;                  // B rows per wave
     constexpr int TN = WTN / 16;                   // 16-col MFMA tiles per wave
     constexpr int AR = BM < 32 ? 32 : BM;          // A rows in LDS (BM 16: rows repeat)
-    constexpr int A_IN = AR / 32;                  // A DMA instructions per wave
-    static_assert(TM >= 1 && TN >= 2 && TN % 2 == 0, "tile shape");
+    constexpr int NA = AR / 8;                     // A DMA instructions (8 rows each)
+    static_assert(TM >= 1 && TN >= 1 && (!SWIGLU || TN % 2 == 0), "tile shape");
     const int wm = wid / WN, wn = wid % WN;
     const int n_valid = min(row_end - row0, BM);   // >= 1
 
@@ -120,25 +125,28 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
 
     // ---- this lane's DMA sources.  A wave instruction fills 1024 LDS bytes = 8 rows
     // of 128 B; lane L lands at row L/8, slot L%8 and fetches global piece
-    // (L%8) ^ (row%8), which realises the XOR swizzle read back below.
-    const uint8_t* a_src[A_IN];
+    // (L%8) ^ swz(row), which realises the XOR swizzle read back below.  A row group q
+    // (rows 8q .. 8q+7) is fetched by wave q % 8.
+    const uint8_t* a_src[A_IN_MAX];
 #pragma unroll
-    for (int i = 0; i < A_IN; ++i) {
-      const int row = (wid * A_IN + i) * 8 + lr8;               // 0 .. AR-1
-      a_src[i] = args.A + (size_t)row_src[row % BM] * K + piece * 16;
+    for (int i = 0; i < A_IN_MAX; ++i) {
+      const int row = ((wid + NW * i) * 8 + lr8) % AR;
+      a_src[i] = args.A + (size_t)row_src[row % BM] * K + (slot ^ swz(row)) * 16;
     }
-    // A row groups holding at least one real row; the rest are never fetched
-    const int a_cnt = min(max((min(n_valid, AR) - wid * A_IN * 8 + 7) / 8, 0), A_IN);
-    const int per = a_cnt + B_IN + 1;               // DMA instructions per stage
+    // row groups holding at least one real row; the rest are never fetched
+    const int groups = min((min(n_valid, AR) + 7) / 8, NA);
+    const int a_cnt = min(max((groups - wid + NW - 1) / NW, 0), A_IN_MAX);
+    const bool has_sc = wid < 3;                    // waves 0/1: sA rows, wave 2: sB
+    const int per = a_cnt + B_IN + (has_sc ? 1 : 0); // DMA instructions per stage
     const size_t nbrows = SWIGLU ? 2 * (size_t)N : (size_t)N;
     const uint8_t* b_src[B_IN];
 #pragma unroll
     for (int i = 0; i < B_IN; ++i) {
       const int row = (wid * B_IN + i) * 8 + lr8;               // 0 .. BNB-1
       const int grow = SWIGLU ? (row < BN_OUT ? n0 + row : N + n0 + row - BN_OUT) : n0 + row;
-      b_src[i] = args.B + ((size_t)g * nbrows + grow) * K + piece * 16;
+      b_src[i] = args.B + ((size_t)g * nbrows + grow) * K + (slot ^ swz(row)) * 16;
     }
-    // scale DMA: waves 0/1 -> sA rows 0..63 / 64..127; waves 2/3 -> sB, lanes < 32 the
+    // scale DMA: waves 0/1 -> sA rows 0..63 / 64..127; wave 2 -> sB, lanes < 32 the
     // first B column block of the tile, lanes >= 32 the second (SwiGLU: gate / up)
     const size_t nbk = nbrows / 128;
     const float* sc_src;
@@ -149,17 +157,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
       if (lane >= 32) nb = SWIGLU ? (N + n0) / 128 : min(n0 / 128 + 1, (int)nbk - 1);
       sc_src = args.sB + ((size_t)g * nbk + nb) * KB;
     }
-    const uint32_t m_a = lds0 + (uint32_t)wid * (A_IN * 1024);
+    const uint32_t m_a = lds0 + (uint32_t)wid * 1024;
     const uint32_t m_b = lds0 + A_BYTES + (uint32_t)wid * (B_IN * 1024);
-    const uint32_t m_s = lds0 + SC_OFF + (uint32_t)wid * 256;
+    const uint32_t m_s = lds0 + SC_OFF + (uint32_t)min(wid, 2) * 256;
     auto issue = [&](int st, int kb) {
       const uint32_t so = (uint32_t)st * STAGE;
 #pragma unroll
-      for (int i = 0; i < A_IN; ++i)
-        if (i < a_cnt) dma16(a_src[i] + (size_t)kb * 128, m_a + so + i * 1024);
+      for (int i = 0; i < A_IN_MAX; ++i)
+        if (i < a_cnt) dma16(a_src[i] + (size_t)kb * 128, m_a + so + i * (NW * 1024));
 #pragma unroll
       for (int i = 0; i < B_IN; ++i) dma16(b_src[i] + (size_t)kb * 128, m_b + so + i * 1024);
-      dma4(sc_src + kb, m_s + so);
+      if (has_sc) dma4(sc_src + kb, m_s + so);
     };
 
     v4f acc[TM][TN];
@@ -187,8 +195,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
         auto read_a = [&](int i) {
           const int row = wm * WTM + i * 16 + (lane & 15);
           const uint8_t* base = L + row * 128;
-          const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ (row & 7)) << 4));
-          const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ (row & 7)) << 4));
+          const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ swz(row)) << 4));
+          const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ swz(row)) << 4));
           af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         };
         auto read_b = [&](int j) {
@@ -200,8 +208,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
             brow = wn * WTN + j * 16 + (lane & 15);
           }
           const uint8_t* base = L + A_BYTES + brow * 128;
-          const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ (brow & 7)) << 4));
-          const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ (brow & 7)) << 4));
+          const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ swz(brow)) << 4));
+          const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ swz(brow)) << 4));
           return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         };
         // promotion scales: sA of this lane's 4 rows per row tile times sB of the
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
       __syncthreads();
       uint8_t* C = static_cast<uint8_t*>(args.C);
       constexpr int CPR = OB / 16;                   // 16-byte chunks per row
-      for (int c = tid; c < n_valid * CPR; c += 256) {
+      for (int c = tid; c < n_valid * CPR; c += NT) {
         const int trow = c / CPR, ch = c % CPR;
         *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) =
             *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            red[wn][wm * WTM + i * 16 + (lane >> 4) * 4 + r] = rmax[i][r];
+            red[wn * BM + wm * WTM + i * 16 + (lane >> 4) * 4 + r] = rmax[i][r];
       }
       __syncthreads();
       if (active) {
@@ -297,9 +305,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int trow = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-            float m = red[0][trow];
+            float m = red[trow];
 #pragma unroll
-            for (int w = 1; w < WN; ++w) m = fmaxf(m, red[w][trow]);
+            for (int w = 1; w < WN; ++w) m = fmaxf(m, red[w * BM + trow]);
             const float s = block_scale(m);
             const float inv = 1.0f / s;
 #pragma unroll
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs args) {
       }
       __syncthreads();
       uint8_t* C = static_cast<uint8_t*>(args.C);
-      for (int c = tid; c < n_valid * 8; c += 256) {
+      for (int c = tid; c < n_valid * 8; c += NT) {
         const int trow = c / 8, ch = c % 8;
         *reinterpret_cast<v4i*>(C + (size_t)(row0 + trow) * N + n0 + ch * 16) =
             *reinterpret_cast<const v4i*>(ot + trow * 128 + ch * 16);
@@ -349,7 +357,7 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_r
   long grid = std::min<long>(mtiles * tiles_n, (long)num_cus);
   if (grid >= 8) grid = grid / 8 * 8;
   if (grid < 1) grid = 1;
-  dim3 gd((unsigned)grid), bd(256);
+  dim3 gd((unsigned)grid), bd(512);
   // bm: tile rows of small groups (16, 32 or 64); groups above it use 128-row tiles
   const int bms = bm >= 64 ? 64 : bm;
 #define MOE_GEMM_CASE(BMSV, BNBV, SW) \

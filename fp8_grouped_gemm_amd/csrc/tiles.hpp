@@ -23,14 +23,15 @@ struct TileMap {
 template <int BMS, int BMB>
 __device__ __forceinline__ int tile_rows(int M) { return M <= BMS ? BMS : BMB; }
 
-template <int BMS, int BMB = BMS>
+template <int BMS, int BMB = BMS, int NT = 256>
 __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int G) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  __shared__ int wsum[4];
-  for (int i = tid; i <= G; i += 256) tm.off[i] = offsets[i];
+  __shared__ int wsum[NW];
+  for (int i = tid; i <= G; i += NT) tm.off[i] = offsets[i];
   __syncthreads();
   // each thread owns a contiguous chunk of groups
-  const int per = (G + 255) / 256;
+  const int per = (G + NT - 1) / NT;
   const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
   int local = 0;
   for (int g = g0; g < g1; ++g) {
@@ -55,7 +56,7 @@ __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets,
     const int bm = tile_rows<BMS, BMB>(M);
     run += (M + bm - 1) / bm;
   }
-  if (tid == 255) tm.start[G] = base + incl;
+  if (tid == NT - 1) tm.start[G] = base + incl;
   __syncthreads();
 }
 
