@@ -20,7 +20,8 @@ from ._lib import (MOE_BF16, MOE_E4M3, MOE_EPI_PLAIN, MOE_EPI_SWIGLU, MOE_F32, M
 __all__ = [
     "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route",
     "moe_route_from_logits", "moe_route_hash", "moe_route_workspace_size", "moe_dispatch", "moe_quant_fp8",
-    "moe_quant_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_w4a16",
+    "moe_quant_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_fp8_masked",
+    "gemm_fp8", "grouped_gemm_w4a16",
     "grouped_gemm_f32", "moe_combine", "moe_layer_workspace_size", "moe_layer_fwd", "MoeError",
     "LayerDesc",
 ]
@@ -183,6 +184,37 @@ def grouped_gemm_fp8(A, sA, B, sB, offsets, R_cap: int, N: int, swiglu: bool = F
                                         _ptr(sB), _ptr(offsets), G, R_cap, N, K, epi, out_dt,
                                         _ptr(Cc), _ptr(sC), _stream(dev)), "grouped_gemm_fp8")
     return (Cc, sC) if swiglu else Cc
+
+
+def grouped_gemm_fp8_masked(A, sA, B, sB, counts, cap: int, N: int, swiglu: bool = False):
+    """Fixed-capacity layout: A [G*cap, K]; group g owns rows [g*cap, g*cap + counts[g]).
+    Returns C bf16 [G*cap, N] (plain) or (codes e4m3 [G*cap, N], sC [G*cap, N/128])."""
+    K = A.shape[1]
+    G = B.shape[0]
+    dev = A.device
+    rows = G * cap
+    if swiglu:
+        Cc = torch.empty((rows, N), dtype=torch.uint8, device=dev)
+        sC = torch.empty((rows, N // 128), dtype=torch.float32, device=dev)
+        out_dt, epi = MOE_E4M3, MOE_EPI_SWIGLU
+    else:
+        Cc = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+        sC = None
+        out_dt, epi = MOE_BF16, MOE_EPI_PLAIN
+    _lib.check(_lib_().grouped_gemm_fp8_masked(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(counts),
+                                               G, cap, N, K, epi, out_dt, _ptr(Cc), _ptr(sC),
+                                               _stream(dev)), "grouped_gemm_fp8_masked")
+    return (Cc, sC) if swiglu else Cc
+
+
+def gemm_fp8(A, sA, B, sB):
+    """Dense block-scaled FP8 GEMM: A [M, K] e4m3 + sA, B [N, K] e4m3 + sB -> bf16 [M, N]."""
+    M, K = A.shape
+    N = B.shape[0]
+    Cc = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _lib.check(_lib_().gemm_fp8(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), M, N, K, _ptr(Cc),
+                                _stream(A.device)), "gemm_fp8")
+    return Cc
 
 
 def grouped_gemm_w4a16(A, B, s7, offsets, R_cap: int, N: int, swiglu: bool = False,

@@ -54,6 +54,8 @@ SIGNATURES = {
     "moe_quant_weight_fp8": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_quant_weight_int4": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "grouped_gemm_fp8": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "grouped_gemm_fp8_masked": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "gemm_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
     "grouped_gemm_w4a16": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "grouped_gemm_f32": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _I, _P, _P, _I, _I, _I, _P, _I, _P]),

@@ -12,6 +12,7 @@
 
 #include "../../include/moe.h"
 #include "launch.hpp"
+#include "tiles.hpp"
 
 namespace {
 
@@ -263,6 +264,47 @@ int grouped_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows, i
   return hip_status(moe::launch_gemm_fp8(A, sA, a_rows, a_row_div, B, sB, offsets, G, R_cap, N, K,
                                          swiglu, C, sC, bm, cus, S(stream)),
                     "grouped_gemm_fp8 launch");
+}
+
+int grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                            const int32_t* counts, int G, int cap, int N, int K, int epilogue,
+                            moe_dtype out_dt, void* C, float* sC, void* stream) {
+  REQUIRE(cap >= 0, "grouped_gemm_fp8_masked: cap must be >= 0");
+  REQUIRE((long long)G * cap < (1LL << 31), "grouped_gemm_fp8_masked: G * cap overflows int32");
+  const int rows = G * cap;
+  int st = v_gemm_common(A, B, counts, G, rows, N, K, epilogue, C);
+  if (st) return st;
+  REQUIRE(sA && sB, "grouped_gemm_fp8_masked: null scale pointer");
+  REQUIRE(N % 128 == 0 && K % 128 == 0,
+          "grouped_gemm_fp8_masked: N and K must be multiples of 128");
+  const bool swiglu = epilogue == MOE_EPI_SWIGLU;
+  if (swiglu) {
+    REQUIRE(out_dt == MOE_E4M3 && sC, "grouped_gemm_fp8_masked: SwiGLU epilogue writes e4m3 + sC");
+  } else {
+    REQUIRE(out_dt == MOE_BF16, "grouped_gemm_fp8_masked: plain epilogue writes bf16");
+  }
+  if (rows == 0) return MOE_OK;
+  int cus = 0;
+  if ((st = current_device(&cus))) return st;
+  return hip_status(moe::launch_gemm_fp8(A, sA, nullptr, 1, B, sB, counts, G, rows, N, K, swiglu,
+                                         C, sC, pick_bm(cap, swiglu), cus, S(stream),
+                                         moe::kRowsMasked, cap),
+                    "grouped_gemm_fp8_masked launch");
+}
+
+int gemm_fp8(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB, int M, int N,
+             int K, uint16_t* C, void* stream) {
+  REQUIRE(B && sB && (M == 0 || (A && sA && C)), "gemm_fp8: null pointer");
+  REQUIRE(M >= 0 && N >= 128 && K >= 128, "gemm_fp8: bad sizes");
+  REQUIRE(N % 128 == 0 && K % 128 == 0, "gemm_fp8: N and K must be multiples of 128");
+  if (M == 0) return MOE_OK;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st) return st;
+  return hip_status(moe::launch_gemm_fp8(A, sA, nullptr, 1, B, sB, nullptr, 1, M, N, K, false, C,
+                                         nullptr, pick_bm(M, false), cus, S(stream),
+                                         moe::kRowsDense, M),
+                    "gemm_fp8 launch");
 }
 
 int grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_rows, int a_row_div, const uint8_t* B,

@@ -49,6 +49,7 @@ struct GemmArgs {
   int K;
   void* C;
   float* sC;
+  int mode, cap;  // GroupRows of the tile map and its C (masked) or M (dense)
 };
 }  // namespace
 
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
   const int G = args.G, K = args.K, N = args.N, KB = K / 128;
   const int tiles_n = N / BN_OUT;
 
-  build_tile_map<BMS, BMB, NT>(tm, args.offsets, G);
+  build_tile_map<BMS, BMB, NT>(tm, args.offsets, G, args.mode, args.cap);
   const int total = tm.start[G] * tiles_n;
   const int P = gridDim.x;
   const int b = blockIdx.x;
@@ -337,20 +338,20 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     const int mt = tm.start[g + 1] - tm.start[g];
     const int local = t - tm.start[g] * tiles_n;
     const int ni = local / mt, mi = local % mt;
-    const int rows = tm.off[g + 1] - tm.off[g];
+    const int rows = group_rows(tm, g), r0 = group_row0(tm, g);
     const int n0 = ni * BN_OUT;
     if (rows <= BMS)
-      run_tile(std::integral_constant<int, BMS>{}, g, tm.off[g] + mi * BMS, tm.off[g + 1], n0);
+      run_tile(std::integral_constant<int, BMS>{}, g, r0 + mi * BMS, r0 + rows, n0);
     else
-      run_tile(std::integral_constant<int, BMB>{}, g, tm.off[g] + mi * BMB, tm.off[g + 1], n0);
+      run_tile(std::integral_constant<int, BMB>{}, g, r0 + mi * BMB, r0 + rows, n0);
   }
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows, int a_row_div,
                            const uint8_t* B, const float* sB, const int32_t* offsets, int G,
                            int R_cap, int N, int K, bool swiglu, void* C, float* sC, int bm,
-                           int num_cus, hipStream_t s) {
-  GemmArgs a{A, sA, a_rows, a_row_div, B, sB, offsets, G, N, K, C, sC};
+                           int num_cus, hipStream_t s, int rows_mode, int cap) {
+  GemmArgs a{A, sA, a_rows, a_row_div, B, sB, offsets, G, N, K, C, sC, rows_mode, cap};
   const bool wide = !swiglu && N % 256 == 0;      // 256 output columns per plain tile
   const long tiles_n = swiglu ? N / 128 : (wide ? N / 256 : N / 128);
   const long mtiles = R_cap / (bm < 128 ? bm : 64) + G;

@@ -29,7 +29,8 @@ hipError_t launch_quant_weight_int4(const float* w, int G, int N, int K, uint8_t
 hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows,
                            int a_row_div, const uint8_t* B, const float* sB,
                            const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
-                           void* C, float* sC, int bm, int num_cus, hipStream_t s);
+                           void* C, float* sC, int bm, int num_cus, hipStream_t s,
+                           int rows_mode = 0, int cap = 0);
 hipError_t launch_gemm_w4a16(const uint16_t* A, const int32_t* a_rows, int a_row_div,
                              const uint8_t* B, const float* s7, const int32_t* offsets, int G,
                              int R_cap, int N, int K, bool swiglu, uint16_t* C, int num_cus,

@@ -1,7 +1,10 @@
-// Persistent tile scheduling over per-group row offsets, shared by the grouped GEMMs.
+// Persistent tile scheduling over per-group row ranges, shared by the grouped GEMMs.
 //
-// Groups own row ranges [offsets[g], offsets[g+1]); each is cut into ceil(M_g / BM)
-// row tiles and every row tile into tiles_n column tiles.  Tiles are numbered group
+// Groups own row ranges given one of three ways (GroupRows): contiguous, from prefix
+// offsets [offsets[g], offsets[g+1]); fixed-capacity ("masked"), rows [g C, g C +
+// counts[g]) of a [G, C] row block per group; dense, a single group of M rows.  Each
+// group is cut into ceil(M_g / BM) row tiles and every row tile into tiles_n column
+// tiles.  Tiles are numbered group
 // by group, column tile by column tile, row tile fastest, so that consecutive tiles
 // share one B column tile (a flattened tile list over all groups, as the global tile
 // scheduler in the MegaMoE walkthrough, discosf.com sec. 3.2, describes).
@@ -13,29 +16,49 @@ namespace moe {
 constexpr int kMaxGroups = 1024;
 
 
+enum GroupRows { kRowsOffsets = 0, kRowsMasked = 1, kRowsDense = 2 };
+
 // Tile bookkeeping shared by the workgroup: per-group row-tile prefix sums.
 struct TileMap {
   int start[kMaxGroups + 1];  // first row tile of each group (exclusive prefix)
-  int off[kMaxGroups + 1];    // copy of offsets
+  int off[kMaxGroups + 1];    // offsets: copy; masked: counts clamped to [0, C]; dense: 0, M
+  int mode, cap;              // GroupRows and C (masked) or M (dense)
 };
+
+// first row and row count of group g
+__device__ __forceinline__ int group_row0(const TileMap& tm, int g) {
+  return tm.mode == kRowsMasked ? g * tm.cap : tm.off[g];
+}
+__device__ __forceinline__ int group_rows(const TileMap& tm, int g) {
+  return tm.mode == kRowsMasked ? tm.off[g] : tm.off[g + 1] - tm.off[g];
+}
 
 // Rows per tile of a group with M rows: BMS for small groups (M <= BMS), BMB otherwise.
 template <int BMS, int BMB>
 __device__ __forceinline__ int tile_rows(int M) { return M <= BMS ? BMS : BMB; }
 
 template <int BMS, int BMB = BMS, int NT = 256>
-__device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int G) {
+__device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int G,
+                               int mode = kRowsOffsets, int cap = 0) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   __shared__ int wsum[NW];
-  for (int i = tid; i <= G; i += NT) tm.off[i] = offsets[i];
+  if (tid == 0) {
+    tm.mode = mode;
+    tm.cap = cap;
+  }
+  for (int i = tid; i <= G; i += NT) {
+    if (mode == kRowsOffsets) tm.off[i] = offsets[i];
+    else if (mode == kRowsMasked) tm.off[i] = i < G ? min(max(offsets[i], 0), cap) : 0;
+    else tm.off[i] = i == 0 ? 0 : cap;
+  }
   __syncthreads();
   // each thread owns a contiguous chunk of groups
   const int per = (G + NT - 1) / NT;
   const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
   int local = 0;
   for (int g = g0; g < g1; ++g) {
-    const int M = tm.off[g + 1] - tm.off[g];
+    const int M = group_rows(tm, g);
     const int bm = tile_rows<BMS, BMB>(M);
     local += (M + bm - 1) / bm;
   }
@@ -52,7 +75,7 @@ __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets,
   int run = base + incl - local;
   for (int g = g0; g < g1; ++g) {
     tm.start[g] = run;
-    const int M = tm.off[g + 1] - tm.off[g];
+    const int M = group_rows(tm, g);
     const int bm = tile_rows<BMS, BMB>(M);
     run += (M + bm - 1) / bm;
   }

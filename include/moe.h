@@ -171,6 +171,24 @@ int grouped_gemm_fp8(const uint8_t *A, const float *sA, const int32_t *a_rows, i
                      int R_cap, int N, int K, int epilogue, moe_dtype out_dt, void *C,
                      float *sC, void *stream);
 
+/* The same GEMM over the fixed-capacity ("masked") expert layout, the second of the
+ * grouped layouts DeepGEMM offers beside the contiguous one (qidao123.com day 3; the
+ * per-expert capacity of mooersco.com sec. 2.5): group g owns rows [g*cap, g*cap +
+ * counts[g]) of A [G*cap, K] (counts on the device, clamped to [0, cap]); sA
+ * [G*cap, K/128]; C and sC have G*cap rows, rows past counts[g] in each block are
+ * unspecified.  No row gather.  B, sB, epilogue, out_dt and sizes as grouped_gemm_fp8. */
+int grouped_gemm_fp8_masked(const uint8_t *A, const float *sA, const uint8_t *B,
+                            const float *sB, const int32_t *counts, int G, int cap, int N,
+                            int K, int epilogue, moe_dtype out_dt, void *C, float *sC,
+                            void *stream);
+
+/* Dense FP8 GEMM with the same block scaling (the dense layout, qidao123.com day 3):
+ * C [M, N] bf16 = A [M, K] e4m3 (sA [M, K/128]) times B [N, K] e4m3 (sB [N/128, K/128])
+ * transposed, promoted per 128-deep K block.  N and K multiples of 128, M >= 0 (M = 0:
+ * nothing is launched, A, sA and C may be null). */
+int gemm_fp8(const uint8_t *A, const float *sA, const uint8_t *B, const float *sB, int M,
+             int N, int K, uint16_t *C, void *stream);
+
 /* Grouped GEMM with int4 weights and bf16 activations: B codes [G, Nb, K/2] and
  * s7 [G, Nb, K/128] are dequantised in-kernel to bf16(fl32(q * s7)) and multiplied with
  * A [*, K] bf16 in fp32.  Row gather and epilogues as grouped_gemm_fp8; output C

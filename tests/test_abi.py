@@ -23,7 +23,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = _lib.load()
     declared = _declared()
-    assert len(declared) == 18, declared
+    assert len(declared) == 20, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -95,6 +95,12 @@ def test_gemm_and_combine_reject_bad_args():
                               _lib.MOE_BF16, FAKE, None, S), "epilogue")
     _err(lib.grouped_gemm_fp8(FAKE, None, None, 1, FAKE, FAKE, FAKE, 2, 128, 128, 128, 0,
                               _lib.MOE_BF16, FAKE, None, S), "scale")
+    _err(lib.grouped_gemm_fp8_masked(FAKE, FAKE, FAKE, FAKE, FAKE, 4, -1, 128, 128, 0,
+                                     _lib.MOE_BF16, FAKE, None, S), "cap")
+    _err(lib.grouped_gemm_fp8_masked(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 128, 100, 0,
+                                     _lib.MOE_BF16, FAKE, None, S), "multiples of 128")
+    _err(lib.gemm_fp8(FAKE, FAKE, FAKE, FAKE, 16, 384, 200, FAKE, S), "multiples of 128")
+    _err(lib.gemm_fp8(None, FAKE, FAKE, FAKE, 16, 128, 128, FAKE, S), "null")
     _err(lib.grouped_gemm_w4a16(FAKE, None, 1, FAKE, FAKE, FAKE, 2, 64, 96, 128, 1, FAKE, S),
          "multiple of 128")
     _err(lib.grouped_gemm_f32(FAKE, None, 1, FAKE, FAKE, 2, 64, 24, 128, 0, FAKE, S),

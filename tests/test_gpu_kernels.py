@@ -265,6 +265,74 @@ def test_grouped_gemm_fp8_row_gather():
     assert beyond <= TOL
 
 
+def _check_swiglu_codes(codes, sc, ref, sab, N):
+    """GPU SwiGLU+requant output against the oracle's h within the MFMA error model:
+    unambiguous codes bit-exact, the rest one of the two correct neighbours."""
+    h, dh = swiglu_error_model(ref[:, :N], ref[:, N:], sab[:, :N], sab[:, N:])
+    q, s, q_lo, q_hi, delta, rho = requant_band(h, dh)
+    assert np.all(np.abs(sc.astype(np.float64) - s) <= s * rho * 1.01)
+    dg = OC.e4m3_decode(codes)
+    ok = (dg >= np.minimum(OC.e4m3_decode(q_lo), OC.e4m3_decode(q_hi))) & \
+         (dg <= np.maximum(OC.e4m3_decode(q_lo), OC.e4m3_decode(q_hi)))
+    unique = q_lo == q_hi
+    np.testing.assert_array_equal(codes[unique], q[unique])
+    assert ok.all()
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_fp8_masked(swiglu):
+    """Fixed-capacity layout: group g owns rows [g*cap, g*cap + min(counts[g], cap))."""
+    G, cap, N, K = 5, 48, 128, 384
+    counts = np.array([0, 1, 48, 60, 17], np.int32)          # 60 > cap: clamped
+    note(f"gemm fp8 masked swiglu={swiglu}")
+    a = synth.normal((G * cap, K), 21, "gemm_a")
+    Nb = 2 * N if swiglu else N
+    b = synth.normal((G, Nb, K), 21, "gemm_b", std=K ** -0.5)
+    qa, sa = M.moe_quant_fp8(a.to(dev()))
+    qb, sb = M.moe_quant_weight_fp8(b.to(dev()))
+    qao, sao = OC.quant_fp8_act(a.numpy())
+    qbo, sbo = OC.quant_fp8_weight(b.numpy())
+    out = M.grouped_gemm_fp8_masked(qa, sa, qb, sb, torch.from_numpy(counts).to(dev()), cap, N,
+                                    swiglu=swiglu)
+    A = OC.dequant_fp8_act(qao, sao)
+    Bd = OC.dequant_fp8_weight(qbo, sbo)
+    for g in range(G):
+        n = int(min(counts[g], cap))
+        if n == 0:
+            continue
+        rows = slice(g * cap, g * cap + n)
+        one = np.array([0, n], np.int32)
+        ref = O.grouped_gemm_fp8(qao[rows], sao[rows], qbo[g:g + 1], sbo[g:g + 1], one)
+        if not swiglu:
+            beyond, raw = error_ratios(to_np(out)[rows], ref)
+            assert beyond <= TOL, (g, beyond)
+        else:
+            sab = O.grouped_gemm(np.abs(A[rows]), np.abs(Bd[g:g + 1]), one)
+            _check_swiglu_codes(to_np(out[0])[rows], to_np(out[1])[rows], ref, sab, N)
+
+
+@pytest.mark.parametrize("Mrows", [0, 1, 200, 333])
+def test_gemm_fp8_dense(Mrows):
+    N, K = 384, 512
+    note(f"gemm fp8 dense M={Mrows}")
+    a = synth.normal((max(Mrows, 1), K), 22, "gemm_a")[:Mrows]
+    b = synth.normal((N, K), 22, "gemm_b", std=K ** -0.5)
+    qa, sa = M.moe_quant_fp8(a.to(dev())) if Mrows else (
+        torch.empty((0, K), dtype=torch.uint8, device=dev()),
+        torch.empty((0, K // 128), dtype=torch.float32, device=dev()))
+    qb, sb = M.moe_quant_weight_fp8(b[None].to(dev()))
+    c = M.gemm_fp8(qa, sa, qb[0], sb[0])
+    assert tuple(c.shape) == (Mrows, N)
+    if Mrows == 0:
+        return
+    qao, sao = OC.quant_fp8_act(a.numpy())
+    qbo, sbo = OC.quant_fp8_weight(b[None].numpy())
+    ref = O.grouped_gemm_fp8(qao, sao, qbo, sbo, np.array([0, Mrows], np.int32))
+    beyond, raw = error_ratios(to_np(c), ref)
+    print(f"beyond={beyond:.3e} raw={raw:.3e}")
+    assert beyond <= TOL
+
+
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_grouped_gemm_w4a16(swiglu):
     sizes = [70, 0, 130, 5]
