@@ -159,7 +159,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_fp8",
-                    choices=sorted(synth.WORKLOADS) + ["grouped_gemm_fp8"])
+                    choices=sorted(synth.WORKLOADS) + ["grouped_gemm_fp8", "dense_gemm_fp8",
+                                                       "masked_gemm_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--trace-summary", metavar="DIR",
@@ -183,6 +184,12 @@ def main(argv=None):
     import fp8_grouped_gemm_amd as M
     if a.workload == "grouped_gemm_fp8":
         print(json.dumps(bench_grouped_gemm(M, a.steps, a.warmup)), flush=True)
+        return 0
+    if a.workload == "dense_gemm_fp8":
+        print(json.dumps(bench_dense_gemm(M, a.steps, a.warmup)), flush=True)
+        return 0
+    if a.workload == "masked_gemm_fp8":
+        print(json.dumps(bench_masked_gemm(M, a.steps, a.warmup)), flush=True)
         return 0
     w = synth.WORKLOADS[a.workload]
     if w.m_align != 16:
@@ -352,6 +359,86 @@ def bench_grouped_gemm(M, steps, warmup):
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
                          "traffic": None}}
+
+
+def _time_flushed(fn, steps, warmup):
+    """Average HIP-event time of fn() with a 512 MB write before each launch (outside the
+    events), so that the weights do not stay in the last-level cache."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    tot = 0.0
+    for _ in range(steps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        tot += e0.elapsed_time(e1)
+    return tot / steps
+
+
+def bench_dense_gemm(M, steps, warmup):
+    """Dense block-scaled FP8 GEMM at the standalone grouped GEMM's size: M=8192, N=4096,
+    K=7168, bf16 out."""
+    dev = torch.device("cuda:0")
+    Mr, N, K = 8192, 4096, 7168
+    a = synth.normal((Mr, K), 0, "gemm_a", device=dev)
+    b = synth.normal((1, N, K), 0, "gemm_b", device=dev, std=K ** -0.5)
+    qa, sa = M.moe_quant_fp8(a)
+    qb, sb = M.moe_quant_weight_fp8(b)
+    ms = _time_flushed(lambda: M.gemm_fp8(qa, sa, qb[0], sb[0]), steps, warmup)
+    tflops = 2.0 * Mr * N * K / (ms * 1e-3) / 1e12
+    return {"metric": "FP8 dense GEMM TFLOPS on 1 MI355X (% roofline)", "value": round(tflops, 1),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+            "config": {"workload": "dense_gemm_fp8: M=8192, N=4096, K=7168, bf16 out"},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                         "traffic": None}}
+
+
+def bench_masked_gemm(M, steps, warmup):
+    """GEMM1 of the decode layer over the fixed-capacity layout: the 128-token decode
+    routing of 256 experts, capacity ceil(T k / E) * 2 rows per expert, SwiGLU + e4m3
+    requant, N = I = 2048, K = d = 7168.  Bound by the touched experts' weight stream."""
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS["decode_fp8"]
+    inp, weights = make_layer(w, dev)
+    idx, _, _ = M.moe_route(inp["x"], inp["w_router"], inp["bias"], w.k)
+    cap = M.moe_capacity(w.T, w.k, w.E, 2.0)
+    counts = torch.bincount(idx.flatten().long(), minlength=w.E).to(torch.int32)
+    qx, sx = M.moe_quant_fp8(inp["x"])
+    rows = w.E * cap
+    # each expert's block: its routed tokens first (any order serves the timing)
+    order = torch.argsort(idx.flatten(), stable=True)
+    e_sorted = idx.flatten()[order].long()
+    first = torch.cumsum(counts.long(), 0) - counts.long()
+    pos = torch.arange(order.numel(), device=dev) - first[e_sorted]
+    keep = pos < cap
+    src = torch.zeros(rows, dtype=torch.int64, device=dev)
+    src[(e_sorted * cap + pos)[keep]] = (order // w.k)[keep]
+    qa, sa = qx[src].contiguous(), sx[src].contiguous()
+    cnt = torch.clamp(counts, max=cap)
+    ms = _time_flushed(lambda: M.grouped_gemm_fp8_masked(qa, sa, weights["w13"], weights["s13"],
+                                                          cnt, cap, w.I, swiglu=True),
+                       steps, warmup)
+    touched = int((cnt > 0).sum().item())
+    wbytes = touched * (2 * w.I * w.d + 2 * w.I // 128 * w.d // 128 * 4)
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    tflops = 2.0 * float(cnt.sum().item()) * 2 * w.I * w.d / (ms * 1e-3) / 1e12
+    return {"metric": "FP8 masked grouped-GEMM weight stream on 1 MI355X (% roofline)",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+            "tflops": round(tflops, 2),
+            "config": {"workload": f"masked_gemm_fp8: decode GEMM1, E=256 x cap {cap}, "
+                                   f"{touched} experts touched, N=2048 (SwiGLU), K=7168"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
 
 
 def stage_times(M, w, inp, weights, steps):
