@@ -177,6 +177,10 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     const bool active = wm * WTM < n_valid;          // wave has a real row
+    // small tiles: 16-row blocks holding a real row; the rest are neither read nor
+    // multiplied (their results are never stored).  Large tiles run every block (a
+    // branch per block costs them more than the rare partial tile saves).
+    const int tmv = BM == BMB ? TM : min(TM, max((n_valid - wm * WTM + 15) / 16, 0));
 
     // K loop: buffers hold blocks kb, kb+1, kb+2 (NS = 3); while block kb is
     // multiplied, kb+1 and kb+2 are in flight.  One barrier per block: it publishes
@@ -225,7 +229,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
         // sets, the next one read while the current one is multiplied
         v8i bcur = read_b(0);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) read_a(i);
+        for (int i = 0; i < TM; ++i)
+          if (i < tmv) read_a(i);
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -234,10 +239,12 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
           v4f pp[TM];
 #pragma unroll
           for (int i = 0; i < TM; ++i)
-            pp[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bcur, zero, 0, 0, 0,
-                                                                    0, 0, 0);
+            if (i < tmv)
+              pp[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bcur, zero, 0, 0,
+                                                                      0, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
+            if (i >= tmv) continue;
             const v4f sc = sa[i] * sb;
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc[r], pp[i][r], acc[i][j][r]);
