@@ -6,8 +6,9 @@
 // An optional capacity keeps the first C slots of each expert and drops the rest
 // silently (DeepSeek MoE architecture, mooersco.com sec. 2.5).
 //
-// One workgroup per expert scans the whole slot list in order, so ranks come from
-// integer prefix counts only: the result does not depend on scheduling.
+// Ranks come from integer counts and lane masks only, so the result does not depend on
+// scheduling.  Up to 512 experts one workgroup does it all (dispatch_fused_kernel);
+// above that, one workgroup per expert scans the whole slot list.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -93,10 +94,116 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   for (int r = all + e * 256 + tid; r < rows_bound; r += E * 256) slot_of_row[r] = -1;
 }
 
+// One workgroup of 16 waves.  Wave w owns the contiguous slot segment [w S, (w+1) S).
+// Pass 1 counts each segment's slots per expert; a scan over experts (padded kept
+// counts) gives the offsets, and a scan over the segments of each expert turns the
+// counts into each segment's first row.  Pass 2 walks every segment in order, 64 slots
+// at a time: a 64-bit mask per expert marks the lanes that chose it, so a slot's rank
+// among them is the popcount of the mask below its lane, and the lowest such lane
+// advances the expert's row.  Slot order inside every expert is thus preserved.
+template <int EMAX>
+__global__ __launch_bounds__(1024) void dispatch_fused_kernel(
+    const int32_t* __restrict__ idx, int n_slots, int E, int m_align, int cap,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_of_slot, int32_t* __restrict__ slot_of_row, int rows_bound) {
+  constexpr int NW = 16;
+  __shared__ int cnt[NW][EMAX];                    // counts, then running row of the segment
+  __shared__ unsigned long long msk[NW][EMAX];
+  __shared__ int off_s[EMAX + 1], kept_s[EMAX];
+  __shared__ int wsum[NW];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < NW * EMAX; i += 1024) {
+    (&cnt[0][0])[i] = 0;
+    (&msk[0][0])[i] = 0ull;
+  }
+  for (int r = tid; r < rows_bound; r += 1024) slot_of_row[r] = -1;
+  __syncthreads();
+  const int seg = (n_slots + NW - 1) / NW;
+  const int s0 = min(w * seg, n_slots), s1 = min(s0 + seg, n_slots);
+  for (int s = s0 + lane; s < s1; s += 64) {
+    const int e = idx[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[w][e], 1);   // other values: dropped
+  }
+  __syncthreads();
+
+  // experts: totals, kept and padded counts, exclusive scan of the padded counts
+  int total = 0, padded = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int v = 0; v < NW; ++v) total += cnt[v][tid];
+    const int kept = cap > 0 ? min(total, cap) : total;
+    padded = (kept + m_align - 1) / m_align * m_align;
+    kept_s[tid] = kept;
+    counts[tid] = total;
+  }
+  int incl = padded;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int v = 0; v < w; ++v) before += wsum[v];
+  const int excl = before + incl - padded;
+  if (tid < E) {
+    off_s[tid] = excl;
+    offsets[tid] = excl;
+    int run = excl;                                // first row of each segment's slots
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const int c = cnt[v][tid];
+      cnt[v][tid] = run;
+      run += c;
+    }
+  }
+  if (tid == E - 1) {
+    off_s[E] = excl + padded;
+    offsets[E] = excl + padded;
+  }
+  __syncthreads();
+
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int sb = s0; sb < s1; sb += 64) {
+    const int s = sb + lane;
+    const int e = s < s1 ? idx[s] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    if (s < s1 && !valid) row_of_slot[s] = -1;
+    if (valid) atomicOr(&msk[w][e], 1ull << lane);
+    const unsigned long long m = valid ? msk[w][e] : 0ull;
+    const int row = valid ? cnt[w][e] + __popcll(m & below) : 0;
+    // the wave's LDS accesses run in order: every lane has read the mask and the row
+    // before the lowest lane of each expert advances and clears them
+    if (valid && (m & below) == 0ull) {
+      cnt[w][e] += __popcll(m);
+      msk[w][e] = 0ull;
+    }
+    if (valid) {
+      if (row - off_s[e] < kept_s[e]) {
+        row_of_slot[s] = row;
+        slot_of_row[row] = s;
+      } else {
+        row_of_slot[s] = -1;
+      }
+    }
+  }
+}
+
 hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int m_align, int cap,
                            int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
                            int32_t* slot_of_row, int rows_bound, hipStream_t s) {
   const int n = T * k;
+  if (E <= 256) {
+    hipLaunchKernelGGL(dispatch_fused_kernel<256>, dim3(1), dim3(1024), 0, s, idx, n, E, m_align,
+                       cap, counts, offsets, row_of_slot, slot_of_row, rows_bound);
+    return hipGetLastError();
+  }
+  if (E <= 512) {
+    hipLaunchKernelGGL(dispatch_fused_kernel<512>, dim3(1), dim3(1024), 0, s, idx, n, E, m_align,
+                       cap, counts, offsets, row_of_slot, slot_of_row, rows_bound);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(E), dim3(256), 0, s, idx, n, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

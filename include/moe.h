@@ -125,7 +125,8 @@ int moe_route_hash(const int64_t *token_ids, int T, int E, int32_t *topk_idx,
  *                     slot order (stable)
  *   slot_of_row [moe_rows_bound(T,k,E,m_align)]  inverse map, -1 on padding rows and
  *                     on every row >= offsets[E]
- * topk_idx [T, k] int32 in [0, E).  1 <= m_align <= 1024; capacity >= 0 (0 = dropless).
+ * topk_idx [T, k] int32 in [0, E) (with E <= 512 a slot outside that range is dropped:
+ * row_of_slot -1, not counted).  1 <= m_align <= 1024; capacity >= 0 (0 = dropless).
  * Integer-only and deterministic. */
 int moe_dispatch(const int32_t *topk_idx, int T, int k, int E, int m_align, int capacity,
                  int32_t *counts, int32_t *offsets, int32_t *row_of_slot,

@@ -163,7 +163,9 @@ def test_hash_route():
 @pytest.mark.parametrize("T,E,k,m_align,cap", [(4096, 256, 8, 128, 0), (128, 256, 8, 16, 0),
                                                (500, 64, 1, 128, 0), (333, 13, 3, 32, 0),
                                                (333, 13, 3, 16, 40), (1, 4, 2, 1, 0),
-                                               (0, 4, 2, 16, 0), (2048, 64, 2, 64, 76)])
+                                               (0, 4, 2, 16, 0), (2048, 64, 2, 64, 76),
+                                               (300, 400, 4, 16, 0), (200, 700, 2, 16, 9),
+                                               (16384, 256, 8, 16, 300)])
 def test_dispatch_bitexact(T, E, k, m_align, cap):
     note(f"dispatch T={T} E={E} k={k} m_align={m_align} cap={cap}")
     idx = synth.random_topk(T, E, k, seed=T + E, skew=1.1) if T else np.zeros((0, k), np.int32)
