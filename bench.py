@@ -230,11 +230,24 @@ def main(argv=None):
     stages = {}
     if not a.no_stages and w.mode == "fp8" and w.route == "score":
         stages = stage_times(M, w, inp, weights, a.steps)
+    elif not a.no_stages and w.mode == "w4a16" and w.route == "hash":
+        stages = stage_times_w4a16(M, w, inp, weights, a.steps)
+    if stages:
         log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
     g1_ms = stages.get("gemm1")
     roofline = None
     traffic = measured_traffic("gemm1") if a.workload == "prefill_fp8" else None
-    if g1_ms:
+    if g1_ms and w.mode == "w4a16":
+        # int4 weights streamed once against T rows: ~430 FLOP/B, above the bf16 ridge
+        # (2500 TFLOP/s / 8 TB/s = 312 FLOP/B), so the bound is the bf16 MFMA peak
+        tf = g["gemm1_flops"] / (g1_ms * 1e-3) / 1e12
+        roofline = {"kernel": "grouped_gemm_w4a16 (GEMM1: gate+up, SwiGLU)",
+                    "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None, "avg_ms": round(g1_ms, 4),
+                    "hbm_gbs": round(g["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9, 1),
+                    "flops_per_launch": g["gemm1_flops"]}
+    elif g1_ms:
         achieved = g["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9
         roofline = {"kernel": "grouped_gemm_fp8 (GEMM1: gate+up, SwiGLU, e4m3 requant)",
                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -468,6 +481,35 @@ def stage_times(M, w, inp, weights, steps):
         torch.cuda.synchronize()
         if it == 0:
             continue        # first pass warms the allocator
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    return {n: acc[n] / steps for n in names}
+
+
+def stage_times_w4a16(M, w, inp, weights, steps):
+    """Stage times of the hash-routed W4A16 layer through the individual C entry points
+    (route_hash -> dispatch -> GEMM1 with the token gather -> GEMM2 -> combine)."""
+    x = inp["x"]
+    names = ["route", "dispatch", "gemm1", "gemm2", "combine"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = {n: 0.0 for n in names}
+    R = M.moe_rows_bound(w.T, w.k, w.E, w.m_align)
+    for it in range(steps + 1):
+        ev[0].record()
+        idx, gw = M.moe_route_hash(inp["token_ids"], w.E)
+        ev[1].record()
+        counts, offsets, ros, sor = M.moe_dispatch(idx, w.E, w.m_align)
+        ev[2].record()
+        h = M.grouped_gemm_w4a16(x, weights["w13"], weights["s13"], offsets, R, w.I,
+                                 swiglu=True, a_rows=sor, a_row_div=w.k)
+        ev[3].record()
+        o = M.grouped_gemm_w4a16(h, weights["w2"], weights["s2"], offsets, R, w.d)
+        ev[4].record()
+        M.moe_combine(o, ros, gw, w.T, w.k)
+        ev[5].record()
+        torch.cuda.synchronize()
+        if it == 0:
+            continue
         for i, n in enumerate(names):
             acc[n] += ev[i].elapsed_time(ev[i + 1])
     return {n: acc[n] / steps for n in names}
