@@ -4,10 +4,11 @@
 // 3.1): one fp32 scale per output channel and 128-wide K block.  The stored codes
 // travel from HBM to LDS untouched (a quarter of the bytes of bf16).  Each wave then
 // expands the codes of its own weight rows in registers, right before the MFMA that
-// consumes them, to bf16(fl32(q * s7)): byte-unpack, float conversion and one FMA
-// u' * s7 - 8 * s7 with u' = q + 8 (exactly fl32(q * s7): 8 * s7 is exact and the FMA
-// rounds once), then the hardware round-to-nearest-even bf16 conversion.  The 16x16x32
-// bf16 MFMA accumulates in fp32; the expansion runs on the vector ALU beside it.
+// consumes them, to bf16(fl32(q * s7)) by a byte-permute table lookup (below): the
+// table holds the eight magnitudes' bf16(fl32(m * s7)), each computed with one fp32
+// rounding and the hardware round-to-nearest-even bf16 conversion, so the lookup gives
+// exactly the dequantised weight.  The 32x32x16 bf16 MFMA accumulates in fp32 (AGPRs);
+// the expansion runs on the vector ALU beside it, software-pipelined one step ahead.
 //
 // Tile: 128 rows x 256 weight rows (plain: 256 output columns, the last column tile
 // possibly half used; SwiGLU: 128 gate + 128 up rows for 128 output columns).  Four
