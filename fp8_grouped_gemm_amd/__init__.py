@@ -20,7 +20,7 @@ from ._lib import (MOE_BF16, MOE_E4M3, MOE_EPI_PLAIN, MOE_EPI_SWIGLU, MOE_F32, M
 __all__ = [
     "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route",
     "moe_route_from_logits", "moe_route_hash", "moe_route_workspace_size", "moe_dispatch", "moe_quant_fp8",
-    "moe_quant_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_fp8_masked",
+    "moe_quant_weight_fp8", "moe_pack_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_fp8_masked",
     "gemm_fp8", "grouped_gemm_w4a16",
     "grouped_gemm_f32", "moe_combine", "moe_layer_workspace_size", "moe_layer_fwd", "MoeError",
     "LayerDesc",
@@ -154,6 +154,17 @@ def moe_quant_weight_fp8(w: torch.Tensor):
     return q, s
 
 
+def moe_pack_weight_fp8(q: torch.Tensor):
+    """e4m3 codes [G, N, K] (or [N, K]) -> the fragment-major layout the FP8 GEMMs read
+    (same shape and byte count; see moe_pack_weight_fp8 in include/moe.h)."""
+    q3 = q if q.dim() == 3 else q[None]
+    G, N, K = q3.shape
+    out = torch.empty_like(q3)
+    _lib.check(_lib_().moe_pack_weight_fp8(_ptr(q3.contiguous()), G, N, K, _ptr(out),
+                                           _stream(q.device)), "moe_pack_weight_fp8")
+    return out if q.dim() == 3 else out[0]
+
+
 def moe_quant_weight_int4(w: torch.Tensor):
     G, N, K = w.shape
     dev = w.device
@@ -168,7 +179,8 @@ def moe_quant_weight_int4(w: torch.Tensor):
 
 def grouped_gemm_fp8(A, sA, B, sB, offsets, R_cap: int, N: int, swiglu: bool = False,
                      a_rows: Optional[torch.Tensor] = None, a_row_div: int = 1):
-    """Returns C bf16 [R_cap, N] (plain) or (codes e4m3 [R_cap, N], sC [R_cap, N/128])."""
+    """B: weight codes packed by moe_pack_weight_fp8.  Returns C bf16 [R_cap, N] (plain)
+    or (codes e4m3 [R_cap, N], sC [R_cap, N/128])."""
     K = A.shape[1]
     G = B.shape[0]
     dev = A.device
@@ -208,7 +220,8 @@ def grouped_gemm_fp8_masked(A, sA, B, sB, counts, cap: int, N: int, swiglu: bool
 
 
 def gemm_fp8(A, sA, B, sB):
-    """Dense block-scaled FP8 GEMM: A [M, K] e4m3 + sA, B [N, K] e4m3 + sB -> bf16 [M, N]."""
+    """Dense block-scaled FP8 GEMM: A [M, K] e4m3 + sA, B [N, K] e4m3 codes packed by
+    moe_pack_weight_fp8 + sB -> bf16 [M, N]."""
     M, K = A.shape
     N = B.shape[0]
     Cc = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)

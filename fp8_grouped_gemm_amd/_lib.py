@@ -52,6 +52,7 @@ SIGNATURES = {
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_quant_fp8": (_I, [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P]),
     "moe_quant_weight_fp8": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_pack_weight_fp8": (_I, [_P, _I, _I, _I, _P, _P]),
     "moe_quant_weight_int4": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "grouped_gemm_fp8": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "grouped_gemm_fp8_masked": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),

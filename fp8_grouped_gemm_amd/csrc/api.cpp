@@ -231,6 +231,17 @@ int moe_quant_weight_fp8(const float* w, int G, int N, int K, uint8_t* q, float*
                     "weight quant launch");
 }
 
+int moe_pack_weight_fp8(const uint8_t* q, int G, int N, int K, uint8_t* qf, void* stream) {
+  REQUIRE(q && qf, "moe_pack_weight_fp8: null pointer");
+  REQUIRE(q != qf, "moe_pack_weight_fp8: q and qf must not overlap");
+  REQUIRE(G >= 1 && G <= 65535, "moe_pack_weight_fp8: G must be in [1, 65535]");
+  REQUIRE(N > 0 && K > 0 && N % 128 == 0 && K % 128 == 0,
+          "moe_pack_weight_fp8: N and K must be positive multiples of 128 (got %d, %d)", N, K);
+  int st = current_device(nullptr);
+  if (st) return st;
+  return hip_status(moe::launch_pack_weight_fp8(q, G, N, K, qf, S(stream)), "fp8 pack launch");
+}
+
 int moe_quant_weight_int4(const float* w, int G, int N, int K, uint8_t* q, float* s7,
                           void* stream) {
   REQUIRE(w && q && s7, "moe_quant_weight_int4: null pointer");
@@ -250,6 +261,8 @@ int grouped_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows, i
   if (st) return st;
   REQUIRE(sA && sB, "grouped_gemm_fp8: null scale pointer");
   REQUIRE(N % 128 == 0 && K % 128 == 0, "grouped_gemm_fp8: N and K must be multiples of 128");
+  REQUIRE(K / 128 <= moe::kGemmMaxKBlocks, "grouped_gemm_fp8: K must be <= %d",
+          128 * moe::kGemmMaxKBlocks);
   REQUIRE(a_row_div >= 1, "grouped_gemm_fp8: a_row_div must be >= 1");
   const bool swiglu = epilogue == MOE_EPI_SWIGLU;
   if (swiglu) {
@@ -277,6 +290,8 @@ int grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B,
   REQUIRE(sA && sB, "grouped_gemm_fp8_masked: null scale pointer");
   REQUIRE(N % 128 == 0 && K % 128 == 0,
           "grouped_gemm_fp8_masked: N and K must be multiples of 128");
+  REQUIRE(K / 128 <= moe::kGemmMaxKBlocks, "grouped_gemm_fp8_masked: K must be <= %d",
+          128 * moe::kGemmMaxKBlocks);
   const bool swiglu = epilogue == MOE_EPI_SWIGLU;
   if (swiglu) {
     REQUIRE(out_dt == MOE_E4M3 && sC, "grouped_gemm_fp8_masked: SwiGLU epilogue writes e4m3 + sC");
@@ -297,6 +312,8 @@ int gemm_fp8(const uint8_t* A, const float* sA, const uint8_t* B, const float* s
   REQUIRE(B && sB && (M == 0 || (A && sA && C)), "gemm_fp8: null pointer");
   REQUIRE(M >= 0 && N >= 128 && K >= 128, "gemm_fp8: bad sizes");
   REQUIRE(N % 128 == 0 && K % 128 == 0, "gemm_fp8: N and K must be multiples of 128");
+  REQUIRE(K / 128 <= moe::kGemmMaxKBlocks, "gemm_fp8: K must be <= %d",
+          128 * moe::kGemmMaxKBlocks);
   if (M == 0) return MOE_OK;
   int cus = 0;
   int st = current_device(&cus);
@@ -374,7 +391,11 @@ int layer_check(const moe_layer_desc* d) {
   REQUIRE(std::isfinite(d->capacity_factor), "moe_layer: capacity_factor must be finite");
   REQUIRE(d->m_align >= 1 && d->m_align <= 1024, "moe_layer: m_align must be in [1, 1024]");
   REQUIRE(d->d % 128 == 0, "moe_layer: d must be a multiple of 128");
-  if (d->mode == MOE_MODE_FP8) REQUIRE(d->I % 128 == 0, "moe_layer: fp8 needs I %% 128 == 0");
+  if (d->mode == MOE_MODE_FP8) {
+    REQUIRE(d->I % 128 == 0, "moe_layer: fp8 needs I %% 128 == 0");
+    REQUIRE(d->d <= 128 * moe::kGemmMaxKBlocks && d->I <= 128 * moe::kGemmMaxKBlocks,
+            "moe_layer: fp8 needs d, I <= %d", 128 * moe::kGemmMaxKBlocks);
+  }
   if (d->mode == MOE_MODE_W4A16) REQUIRE(d->I % 128 == 0, "moe_layer: w4a16 needs I %% 128 == 0");
   if (d->mode == MOE_MODE_FP32) REQUIRE(d->I % 16 == 0, "moe_layer: fp32 needs I %% 16 == 0");
   REQUIRE((long long)d->T * d->k + (long long)d->E * (d->m_align - 1) < (1LL << 31),

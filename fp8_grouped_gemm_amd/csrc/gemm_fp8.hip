@@ -8,30 +8,39 @@
 // the fp32 accumulator with its two scales (the two-level accumulation of DeepGEMM's
 // release notes, qidao123.com day 3).  The output is rounded to bf16 (RNE, walkthrough
 // sec. 3.3) or, with the SwiGLU epilogue, silu(gate)*up is requantised to e4m3 1x128
-// in registers (epilogue fusion, walkthrough sec. 3.2).
+// (epilogue fusion, walkthrough sec. 3.2).
 //
 // gfx950 mapping
 //   * v_mfma_f32_16x16x128_f8f6f4: one instruction covers one 16x16 output tile over
 //     exactly one 128-deep scale block, so promotion is one fp32 FMA per output per
 //     block: acc += (sA*sB) * mfma(a, b, 0).
-//   * 512 threads = 8 wave64s (two per SIMD) over a BM x BNB tile (BNB rows of B).
-//     Prefill tiles are 128 x 256 with 64 x 64 per wave, so one weight byte brought
-//     into LDS feeds 128 token rows and every fragment read from LDS feeds 4 MFMAs.  A SwiGLU tile
-//     loads 128 gate rows and 128 up rows of B so the 1x128 requant block is complete
-//     inside one workgroup.
-//   * Operands reach LDS by direct global->LDS DMA into 3 buffers (two K blocks in
-//     flight), in a 16-byte XOR swizzle (row stride 128 B) read back conflict-free.
-//     Row groups past the end of the group are not fetched and waves whose rows are all
-//     padding skip their MFMAs, so small groups cost little more than their weights.
-//   * Persistent grid: workgroup b works on tiles v, v+P, v+2P, ... where
-//     v = (b mod 8) * P/8 + b/8, so consecutive tiles -- the row tiles that share one
-//     B column tile -- run on the same XCD and share its L2.
+//   * 512 threads = 8 wave64s, two per SIMD: the promotion arithmetic of one wave runs
+//     while the other wave's MFMAs occupy the matrix core.  A workgroup tile is BM rows x
+//     256 weight rows (plain: 256 output columns; SwiGLU: 128 gate + 128 up rows, so the
+//     1x128 requant block is complete in one workgroup).  The waves split the weight rows
+//     (32 each) and all share the BM activation rows.
+//   * Weights are stored fragment-major (moe_pack_weight_fp8): the 2 KB a wave needs
+//     for one 16-row x 128-deep fragment are contiguous, in the order the MFMA takes
+//     them, and go straight from memory to registers -- no LDS traffic, fully coalesced
+//     loads, three K blocks in flight per wave.
+//   * Activation rows (gathered through a_rows) reach LDS by direct global->LDS DMA into
+//     four stages, in a 16-byte XOR swizzle read back conflict-free.  One barrier per K
+//     block, placed two fragment steps before the block ends; the reads of those last
+//     steps already fetch the next block's first fragments, so the MFMAs never wait on
+//     the barrier.
+//   * The tile's activation scales for all K blocks are transposed into LDS once per
+//     tile, so that the K loop loads no scattered scale words.
+//   * Persistent grid; workgroup b works on tiles v, v+P, ... with v = (b mod 8) * P/8 +
+//     b/8, so that the 32 tiles one XCD holds at a time are consecutive; inside a group
+//     they run down up to 8 row tiles before moving to the next column tile, so those 32
+//     tiles share about 8 activation row tiles and 4 weight column tiles in that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 #include "tiles.hpp"
-#include "dma.hpp"
 
 namespace moe {
 
@@ -41,7 +50,7 @@ struct GemmArgs {
   const float* sA;
   const int32_t* a_rows;
   int a_row_div;
-  const uint8_t* B;
+  const uint8_t* Bf;  // fragment-major weights
   const float* sB;
   const int32_t* offsets;
   int G;
@@ -51,124 +60,169 @@ struct GemmArgs {
   float* sC;
   int mode, cap;  // GroupRows of the tile map and its C (masked) or M (dense)
 };
+
+// LDS DMA with a scalar base address and a 32-bit lane offset (see dma.hpp for why the
+// DMA is written as inline asm).
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t m) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+// wait for this wave's LDS operations, then for the whole workgroup
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 }  // namespace
 
-// Two tile classes share one persistent tile list: groups with at most BMS rows are
-// cut into BMS-row tiles worked by 8 waves side by side (all SIMDs busy, the weight
-// stream dominates), larger groups into 128-row tiles worked by 2 x 4 waves (a weight
-// byte in LDS feeds 128 rows).  B tile: BNB rows (SWIGLU: BNB/2 gate + BNB/2 up rows ->
-// BNB/2 output columns; plain: BNB output columns).  Eight waves, two per SIMD, so that
-// one wave's MFMAs cover the other's LDS reads and promotion arithmetic.
-template <int BMS, int BNB, bool SWIGLU>
-__global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
-  constexpr int NT = 512, NW = 8;
-  constexpr int NS = 3;
-  constexpr int BMB = 128;                         // rows of a big-group tile
-  constexpr int BN_OUT = SWIGLU ? BNB / 2 : BNB;   // output columns per tile
-  constexpr int B_IN = BNB / 8 / NW;               // B DMA instructions per wave (8 rows each)
-  constexpr int A_IN_MAX = BMB / 8 / NW;           // A DMA instructions per wave, at most
-  constexpr int PER_MAX = A_IN_MAX + B_IN + 1;     // + one scale load
-  constexpr int A_BYTES = BMB * 128, B_BYTES = BNB * 128;
-  constexpr int SC_OFF = A_BYTES + B_BYTES;        // 4 x 256 B of scale slots
-  constexpr int STAGE = SC_OFF + 1024;
-  static_assert(!SWIGLU || BN_OUT == 128, "1x128 requant block");
-  static_assert(B_IN >= 1 && A_IN_MAX >= 1 && PER_MAX < 16, "DMA split");
+// Fragment-major weight layout: B [G][R][K] e4m3 -> Bf [G][R/16][K/128][2][64][16 B],
+// where half h and lane l of fragment (nb, kb) hold
+// B[16 nb + (l & 15)][128 kb + 32 (l >> 4) + 16 h .. +16] -- the 16x128 operand of one
+// 16x16x128 MFMA, as lane l reads it (rows by lane & 15, 32-byte K chunks by lane >> 4).
+__global__ void pack_weight_fp8_kernel(const uint8_t* __restrict__ B, uint8_t* __restrict__ Bf,
+                                       int G, int R, int K) {
+  const size_t total = (size_t)G * R * (size_t)(K / 16);
+  const int KB = K / 128, R16 = R / 16;
+  for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+       p += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(p % 64);
+    size_t q = p / 64;
+    const int h = (int)(q % 2);
+    q /= 2;
+    const int kb = (int)(q % KB);
+    q /= KB;
+    const int nb = (int)(q % R16);
+    const size_t g = q / R16;
+    const int row = nb * 16 + (l & 15);
+    const int k = kb * 128 + 32 * (l >> 4) + 16 * h;
+    *reinterpret_cast<v4i*>(Bf + p * 16) =
+        *reinterpret_cast<const v4i*>(B + (g * R + row) * (size_t)K + k);
+  }
+}
 
+hipError_t launch_pack_weight_fp8(const uint8_t* B, int G, int R, int K, uint8_t* Bf,
+                                  hipStream_t s) {
+  const size_t pieces = (size_t)G * R * (size_t)(K / 16);
+  const size_t blocks = std::min<size_t>((pieces + 255) / 256, 16384);
+  hipLaunchKernelGGL(pack_weight_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, B, Bf, G,
+                     R, K);
+  return hipGetLastError();
+}
+
+// Two tile classes share one persistent tile list: groups with at most BMS rows get
+// BMS-row tiles (their cost is the weight stream), larger groups 128-row tiles.
+template <int BMS, bool SWIGLU>
+__global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
+  constexpr int NW = 8, NT = 512, BMB = 128, TN = 2;
+  constexpr int BN_OUT = SWIGLU ? 128 : 256;       // output columns per tile
+  constexpr int WB = (SWIGLU ? 128 : 256) / NW;    // weight rows per wave (per half: SwiGLU)
+  constexpr int DB = 3;                            // weight ring: blocks kb .. kb+2
+  constexpr int A_STAGE = BMB * 128;               // activation codes of one K block
+  constexpr int NSA = 4;                           // activation stages
+  constexpr int TAB_OFF = NSA * A_STAGE;           // row-scale table [kb][row]
+  constexpr int STAGE_BYTES = TAB_OFF + kGemmMaxKBlocks * BMB * 4;
+  constexpr int OUT_BYTES = SWIGLU ? BMB * 132 * 4 : BMB * 512;
+  constexpr int LDS_BYTES = STAGE_BYTES > OUT_BYTES ? STAGE_BYTES : OUT_BYTES;
   __shared__ TileMap tm;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS][STAGE];
-  __shared__ float red[SWIGLU ? 512 : 1];          // SwiGLU row maxima [wn][row]
-  __shared__ int row_src[128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  __shared__ int row_src[BMB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = args.G, K = args.K, N = args.N, KB = K / 128;
-  const int tiles_n = N / BN_OUT;
+  const int tiles_n = (N + BN_OUT - 1) / BN_OUT;
+  const int R = SWIGLU ? 2 * N : N;                // weight rows per group
+  const int R16 = R / 16, RB = R / 128;
+  const uint32_t lds0 = lds_addr(lds);
+  const int gsel = 2 * (lane >> 4);
+  // 16-byte piece p of LDS row r sits in slot p ^ swz(r); pairs of 128-byte rows share a
+  // 256-byte bank line, so the key changes every second row
+  auto swz = [](int r) { return (r >> 1) & 7; };
 
   build_tile_map<BMS, BMB, NT>(tm, args.offsets, G, args.mode, args.cap);
   const int total = tm.start[G] * tiles_n;
-  const int P = gridDim.x;
-  const int b = blockIdx.x;
+  const int P = gridDim.x, b = blockIdx.x;
   const int v = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
-  const uint32_t lds0 = lds_addr(&lds[0][0]);
-  const int lr8 = lane >> 3, slot = lane & 7;
-  // 16-byte piece p of row r sits in slot p ^ swz(r) of the row's 128 LDS bytes; pairs
-  // of rows share a 256-byte bank line, so the key changes every second row
-  auto swz = [](int r) { return (r >> 1) & 7; };
-  const int gsel = 2 * (lane >> 4);
 
-  // one tile of class BM (WM waves along M)
   auto run_tile = [&](auto BMC, int g, int row0, int row_end, int n0) {
     constexpr int BM = decltype(BMC)::value;
-    constexpr int WM = BM == BMB ? 2 : 1;
-    constexpr int WN = NW / WM;
-    constexpr int WTM = BM / WM;                   // rows per wave
-    constexpr int TM = WTM / 16;                   // 16-row MFMA tiles per wave
-    constexpr int WTN = BNB / WN;                  // B rows per wave
-    constexpr int TN = WTN / 16;                   // 16-col MFMA tiles per wave
-    constexpr int AR = BM < 32 ? 32 : BM;          // A rows in LDS (BM 16: rows repeat)
-    constexpr int NA = AR / 8;                     // A DMA instructions (8 rows each)
-    static_assert(TM >= 1 && TN >= 1 && (!SWIGLU || TN % 2 == 0), "tile shape");
-    const int wm = wid / WN, wn = wid % WN;
+    constexpr int TM = BM / 16;                    // 16-row MFMA tiles per wave
     const int n_valid = min(row_end - row0, BM);   // >= 1
-
-    // source row of every tile row (gather through a_rows); rows past the group's end
-    // repeat its last row, their results are discarded
-    if (tid < 128) {
-      int lr = min(row0 + (tid % BM), row_end - 1);
+    const int ncols = min(BN_OUT, N - n0);         // plain N % 256 == 128: half last tile
+    if (tid < BM) {
+      // source row of every tile row; rows past the group's end repeat its last row and
+      // their results are discarded
+      const int lr = min(row0 + tid, row_end - 1);
       int src = lr;
       if (args.a_rows) {
-        int sr = args.a_rows[lr];
+        const int sr = args.a_rows[lr];
         src = sr < 0 ? 0 : sr / args.a_row_div;
       }
       row_src[tid] = src;
     }
     __syncthreads();
 
-    // ---- this lane's DMA sources.  A wave instruction fills 1024 LDS bytes = 8 rows
-    // of 128 B; lane L lands at row L/8, slot L%8 and fetches global piece
-    // (L%8) ^ swz(row), which realises the XOR swizzle read back below.  A row group q
-    // (rows 8q .. 8q+7) is fetched by wave q % 8.
-    const uint8_t* a_src[A_IN_MAX];
+    // ---- activation DMA: an instruction fills 8 rows (1 KB); lane L lands at row L/8,
+    // slot L%8 and fetches global piece (L%8) ^ swz(row).  Every wave issues ADMA
+    // instructions per block (small tiles repeat row groups, same bytes to same place).
+    constexpr int GROUPS = BM / 8;
+    constexpr int ADMA = GROUPS > NW ? GROUPS / NW : 1;
+    uint32_t a_voff[ADMA], a_m[ADMA];
 #pragma unroll
-    for (int i = 0; i < A_IN_MAX; ++i) {
-      const int row = ((wid + NW * i) * 8 + lr8) % AR;
-      a_src[i] = args.A + (size_t)row_src[row % BM] * K + (slot ^ swz(row)) * 16;
+    for (int q = 0; q < ADMA; ++q) {
+      const int grp = (wid + NW * q) % GROUPS;
+      const int row = grp * 8 + (lane >> 3), slot = lane & 7;
+      a_voff[q] = (uint32_t)row_src[row] * (uint32_t)K + ((slot ^ swz(row)) << 4);
+      a_m[q] = grp * 1024;
     }
-    // row groups holding at least one real row; the rest are never fetched
-    const int groups = min((min(n_valid, AR) + 7) / 8, NA);
-    const int a_cnt = min(max((groups - wid + NW - 1) / NW, 0), A_IN_MAX);
-    const bool has_sc = wid < 3;                    // waves 0/1: sA rows, wave 2: sB
-    const int per = a_cnt + B_IN + (has_sc ? 1 : 0); // DMA instructions per stage
-    const size_t nbrows = SWIGLU ? 2 * (size_t)N : (size_t)N;
-    const uint8_t* b_src[B_IN];
+    auto dma_a = [&](int kb) {
+      const uint32_t st = lds0 + (uint32_t)(kb % NSA) * A_STAGE;
+      const uint8_t* base = args.A + (size_t)min(kb, KB - 1) * 128;
 #pragma unroll
-    for (int i = 0; i < B_IN; ++i) {
-      const int row = (wid * B_IN + i) * 8 + lr8;               // 0 .. BNB-1
-      const int grow = SWIGLU ? (row < BN_OUT ? n0 + row : N + n0 + row - BN_OUT) : n0 + row;
-      b_src[i] = args.B + ((size_t)g * nbrows + grow) * K + (slot ^ swz(row)) * 16;
+      for (int q = 0; q < ADMA; ++q) dma16s(a_voff[q], base, st + a_m[q]);
+    };
+
+    // ---- the tile's row scales, transposed into LDS [kb][row]: thread (row, q) fetches
+    // blocks 4q .. 4q+3 of one row
+    {
+      float* tab = reinterpret_cast<float*>(lds + TAB_OFF);
+      const int nq = (KB + 3) / 4;
+      for (int p = tid; p < BM * nq; p += NT) {
+        const int row = p % BM, q = p / BM;
+        const float* src = args.sA + (size_t)row_src[row] * KB;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kb = min(4 * q + t, KB - 1);
+          tab[kb * BMB + row] = src[kb];
+        }
+      }
     }
-    // scale DMA: waves 0/1 -> sA rows 0..63 / 64..127; wave 2 -> sB, lanes < 32 the
-    // first B column block of the tile, lanes >= 32 the second (SwiGLU: gate / up)
-    const size_t nbk = nbrows / 128;
-    const float* sc_src;
-    if (wid < 2) {
-      sc_src = args.sA + (size_t)row_src[(wid * 64 + lane) % BM] * KB;
-    } else {
-      int nb = n0 / 128;
-      if (lane >= 32) nb = SWIGLU ? (N + n0) / 128 : min(n0 / 128 + 1, (int)nbk - 1);
-      sc_src = args.sB + ((size_t)g * nbk + nb) * KB;
-    }
-    const uint32_t m_a = lds0 + (uint32_t)wid * 1024;
-    const uint32_t m_b = lds0 + A_BYTES + (uint32_t)wid * (B_IN * 1024);
-    const uint32_t m_s = lds0 + SC_OFF + (uint32_t)min(wid, 2) * 256;
-    auto issue = [&](int st, int kb) {
-      const uint32_t so = (uint32_t)st * STAGE;
+
+    // ---- this wave's weight fragments: a scalar base plus the lane's 16-byte offset.
+    // Waves past a half last tile repeat valid rows; their results are not stored.
+    const int wcol = WB * wid < ncols ? WB * wid : 0;
+    const int brow0 = n0 + wcol;
+    const uint8_t* b_base = args.Bf + (((size_t)g * R16 + brow0 / 16) * (size_t)KB) * 2048;
+    const size_t b_step = (size_t)KB * 2048;       // next 16-row block
+    // plain: fragment j is block j; SwiGLU: j = 0 gate, j = 1 the up row N further on
+    const size_t b_next = SWIGLU ? (size_t)(N / 16) * b_step : b_step;
+    const uint32_t b_lane = lane * 16;
+    const float* sb0 = args.sB + ((size_t)g * RB + brow0 / 128) * KB;
+    const float* sb1 = args.sB + ((size_t)g * RB + (SWIGLU ? (N + brow0) / 128 : 0)) * KB;
+    constexpr int NB_OPS = 2 * TN + (SWIGLU ? 2 : 1);   // vector loads per load_b
+
+    v8i bq[DB][TN];
+    float sbq[DB][2];
+    auto load_b = [&](int slot, int kb) {
+      kb = min(kb, KB - 1);
 #pragma unroll
-      for (int i = 0; i < A_IN_MAX; ++i)
-        if (i < a_cnt) dma16(a_src[i] + (size_t)kb * 128, m_a + so + i * (NW * 1024));
-#pragma unroll
-      for (int i = 0; i < B_IN; ++i) dma16(b_src[i] + (size_t)kb * 128, m_b + so + i * 1024);
-      if (has_sc) dma4(sc_src + kb, m_s + so);
+      for (int j = 0; j < TN; ++j) {
+        const uint8_t* p = b_base + (size_t)j * b_next + (size_t)kb * 2048;
+        const v4i lo = *reinterpret_cast<const v4i*>(p + b_lane);
+        const v4i hi = *reinterpret_cast<const v4i*>(p + 1024 + b_lane);
+        bq[slot][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      sbq[slot][0] = sb0[kb];
+      sbq[slot][1] = SWIGLU ? sb1[kb] : 0.f;
     };
 
     v4f acc[TM][TN];
@@ -176,219 +230,257 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    const bool active = wm * WTM < n_valid;          // wave has a real row
-    // small tiles: 16-row blocks holding a real row; the rest are neither read nor
-    // multiplied (their results are never stored).  Large tiles run every block (a
-    // branch per block costs them more than the rare partial tile saves).
-    const int tmv = BM == BMB ? TM : min(TM, max((n_valid - wm * WTM + 15) / 16, 0));
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-    // K loop: buffers hold blocks kb, kb+1, kb+2 (NS = 3); while block kb is
-    // multiplied, kb+1 and kb+2 are in flight.  One barrier per block: it publishes
-    // block kb and certifies every wave is done with block kb-1, whose buffer is refilled.
-    issue(0, 0);
-    if (KB > 1) issue(1, 1);
-    int st = 0;
-    for (int kb = 0; kb < KB; ++kb) {
-      wait_vmcnt_upto<PER_MAX>(kb + 1 < KB ? per : 0);
-      __builtin_amdgcn_s_barrier();
-      if (kb + 2 < KB) issue(st == 0 ? 2 : st - 1, kb + 2);    // buffer (kb+2) % 3
-      if (active) {
-        const uint8_t* L = lds[st];
-        const float* lsa = reinterpret_cast<const float*>(L + SC_OFF);
-        const float* lsb = reinterpret_cast<const float*>(L + SC_OFF + 512);
-        v8i af[TM];
-        auto read_a = [&](int i) {
-          const int row = wm * WTM + i * 16 + (lane & 15);
-          const uint8_t* base = L + row * 128;
-          const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ swz(row)) << 4));
-          const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ swz(row)) << 4));
-          af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        };
-        auto read_b = [&](int j) {
-          int brow;
-          if (SWIGLU) {
-            const int half = j / (TN / 2), jj = j % (TN / 2);
-            brow = half * BN_OUT + wn * (WTN / 2) + jj * 16 + (lane & 15);
+    // A fragments and their row scales run RA steps ahead of their MFMAs through rings of
+    // AR sets; the reads of a block's last RA steps fetch the next block's first
+    // fragments, published by the barrier RA steps before the block ends.  Promotion of
+    // a step's partials runs one step behind its MFMAs (rings of PR), across blocks.
+    // Ring phases are compile-time because the K loop is unrolled by DB = 3 blocks.
+    constexpr int RA = TM < 2 ? TM : 2;
+    constexpr int AR = 3;                          // divides DB * TM
+    constexpr int PR = (TM % 2 == 0) ? 2 : 3;      // divides DB * TM
+    v8i af[AR];
+    v4f sa[AR];
+    v4f pp[PR][TN];
+    v4f cq[PR][2];
+    auto rd_a = [&](const uint8_t* L, int i) {
+      const int row = i * 16 + (lane & 15);
+      const uint8_t* base = L + row * 128;
+      const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ swz(row)) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ swz(row)) << 4));
+      return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto rd_s = [&](int kbx, int i) {
+      return *reinterpret_cast<const v4f*>(lds + TAB_OFF +
+                                           (kbx * BMB + i * 16 + (lane >> 4) * 4) * 4);
+    };
+    auto promote = [&](int slot, int ii) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v4f c = cq[slot][(SWIGLU && j >= TN / 2) ? 1 : 0];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ii][j][r] = fmaf(c[r], pp[slot][j][r], acc[ii][j][r]);
+      }
+    };
+
+    // one K block.  Vector memory order per block: weights of block kb+2, then the
+    // activation DMA of block kb+3 into the stage block kb-1 used (every wave finished
+    // that stage before the previous block's barrier).
+    auto body = [&](auto U, int kb) {
+      constexpr int u = decltype(U)::value;
+      constexpr int g0 = u * TM;                   // step index within the unrolled round
+      load_b((u + DB - 1) % DB, kb + DB - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      dma_a(kb + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* L = lds + (kb % NSA) * A_STAGE;
+      const uint8_t* Ln = lds + ((kb + 1) % NSA) * A_STAGE;
+      const float sbA = sbq[u][0], sbB = SWIGLU ? sbq[u][1] : sbq[u][0];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int gs = g0 + i;
+        if (i == TM - RA) {
+          // this wave's DMA of block kb+1 (issued two blocks ago) has landed: after it
+          // came the weights of kb+1 and kb+2 and the DMAs of kb+2 and kb+3.  The barrier
+          // publishes block kb+1; every wave's reads of stage kb%NSA before it are done.
+          wait_vmcnt<2 * NB_OPS + 2 * ADMA>();
+          lds_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        {
+          const int ni = i + RA;
+          const int slot = (gs + RA) % AR;
+          if (ni < TM) {
+            af[slot] = rd_a(L, ni);
+            sa[slot] = rd_s(kb, ni);
           } else {
-            brow = wn * WTN + j * 16 + (lane & 15);
+            af[slot] = rd_a(Ln, ni - TM);
+            sa[slot] = rd_s(min(kb + 1, KB - 1), ni - TM);
           }
-          const uint8_t* base = L + A_BYTES + brow * 128;
-          const v4i lo = *reinterpret_cast<const v4i*>(base + ((gsel ^ swz(brow)) << 4));
-          const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ swz(brow)) << 4));
-          return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        };
-        // promotion scales: sA of this lane's 4 rows per row tile times sB of the
-        // column block (plain: this wave's block; SwiGLU: gate for j < TN/2, up after)
-        const float sbA = SWIGLU ? lsb[0] : lsb[wn * WTN >= 128 ? 32 : 0];
-        const float sbB = lsb[32];
-        v4f sa[TM];
+        }
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          sa[i] = *reinterpret_cast<const v4f*>(&lsa[wm * WTM + i * 16 + (lane >> 4) * 4]);
-        // the A fragments stay in registers; B column tiles stream through two register
-        // sets, the next one read while the current one is multiplied
-        v8i bcur = read_b(0);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          if (i < tmv) read_a(i);
-        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j)
+          pp[gs % PR][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[gs % AR], bq[u][j], zero, 0, 0, 0, 0, 0, 0);
+        cq[gs % PR][0] = sa[gs % AR] * sbA;
+        cq[gs % PR][1] = sa[gs % AR] * sbB;
+        // the previous step's partials (before the tile's first block: zeros)
+        promote((gs + DB * TM - 1) % PR, i > 0 ? i - 1 : TM - 1);
+        // issue order inside a step: next fragment's reads, then each MFMA followed by
+        // four promotion FMAs that run in its shadow; nothing moves across steps
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const v8i bnext = (j + 1 < TN) ? read_b(j + 1) : bcur;
-          const float sb = (SWIGLU && j >= TN / 2) ? sbB : sbA;
-          v4f pp[TM];
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-            if (i < tmv)
-              pp[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bcur, zero, 0, 0,
-                                                                      0, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            if (i >= tmv) continue;
-            const v4f sc = sa[i] * sb;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc[r], pp[i][r], acc[i][j][r]);
-          }
-          bcur = bnext;
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      st = st == NS - 1 ? 0 : st + 1;
-    }
+    };
 
-    // ---- epilogue.  MFMA C layout: lane holds column lane%16, rows 4*(lane/16)+r.  The
-    // tile is staged through LDS (every DMA has landed, the stage buffers are free) so
-    // that global stores are 16 contiguous bytes per lane.
-    uint8_t* ot = &lds[0][0];
+    // prologue, in the steady-state order (weights of x, activations of x+1): block 0's
+    // activations in LDS, weights of blocks 0 and 1 and activations of 1 and 2 in flight,
+    // the first RA fragments of block 0 in registers
+    dma_a(0);
+    load_b(0, 0);
+    dma_a(1);
+    load_b(1, 1);
+    dma_a(2);
+    wait_vmcnt<2 * NB_OPS + 2 * ADMA>();
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      af[i] = rd_a(lds, i);
+      sa[i] = rd_s(0, i);
+    }
+#pragma unroll
+    for (int p = 0; p < PR; ++p) {
+      cq[p][0] = zero;
+      cq[p][1] = zero;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) pp[p][j] = zero;
+    }
+    int kb = 0;
+    for (; kb + DB <= KB; kb += DB) {
+      body(std::integral_constant<int, 0>{}, kb);
+      body(std::integral_constant<int, 1>{}, kb + 1);
+      body(std::integral_constant<int, 2>{}, kb + 2);
+    }
+    if (kb < KB) body(std::integral_constant<int, 0>{}, kb);
+    if (kb + 1 < KB) body(std::integral_constant<int, 1>{}, kb + 1);
+    {
+      // the last block's last step
+      const int glast = ((KB - 1) % DB) * TM + TM - 1;
+      if (glast % PR == 0) promote(0, TM - 1);
+      else if (glast % PR == 1) promote(1, TM - 1);
+      else if constexpr (PR > 2) promote(2, TM - 1);
+    }
+    wait_vmcnt<0>();  // the last (clamped) activation DMAs land before LDS is reused
+    lds_barrier();
+
+    // ---- epilogue.  MFMA C layout: lane holds column lane%16, rows 4*(lane/16)+r.
     if constexpr (!SWIGLU) {
-      constexpr int OB = BNB * 2;                    // bytes per staged row
-      __syncthreads();
-      if (active) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int trow = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const int tcol = wn * WTN + j * 16 + (lane & 15);
-              *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(acc[i][j][r]);
-            }
-          }
-      }
-      __syncthreads();
-      uint8_t* C = static_cast<uint8_t*>(args.C);
-      constexpr int CPR = OB / 16;                   // 16-byte chunks per row
-      for (int c = tid; c < n_valid * CPR; c += NT) {
-        const int trow = c / CPR, ch = c % CPR;
-        *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) =
-            *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
-      }
-    } else {
-      constexpr int TH = TN / 2;
-      float h[TM][TH][4];
-      float rmax[TM][4];
+      // bf16 tile staged through LDS for 16-byte stores
+      constexpr int OB = 512;
+      uint8_t* ot = lds;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float m = 0.f;
+          const int trow = i * 16 + (lane >> 4) * 4 + r;
 #pragma unroll
-          for (int j = 0; j < TH; ++j) {
-            h[i][j][r] = silu_fast(acc[i][j][r]) * acc[i][j + TH][r];
-            m = fmaxf(m, fabsf(h[i][j][r]));
+          for (int j = 0; j < TN; ++j) {
+            const int tcol = wid * WB + j * 16 + (lane & 15);
+            *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(acc[i][j][r]);
           }
-          rmax[i][r] = group_max<16>(m);  // across the 16 columns of the MFMA tile
         }
-      if ((lane & 15) == 0) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            red[wn * BM + wm * WTM + i * 16 + (lane >> 4) * 4 + r] = rmax[i][r];
-      }
-      __syncthreads();
-      if (active) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int trow = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-            float m = red[trow];
-#pragma unroll
-            for (int w = 1; w < WN; ++w) m = fmaxf(m, red[w * BM + trow]);
-            const float s = block_scale(m);
-            const float inv = 1.0f / s;
-#pragma unroll
-            for (int j = 0; j < TH; ++j) {
-              const int tcol = wn * (WTN / 2) + j * 16 + (lane & 15);
-              ot[trow * 128 + tcol] = (uint8_t)(e4m3x2(clamp448(h[i][j][r] * inv), 0.f) & 0xFF);
-            }
-            const int row = row0 + trow;
-            if (wn == 0 && (lane & 15) == 0 && row < row_end)
-              args.sC[(size_t)row * (N / 128) + n0 / 128] = s;
-          }
-      }
       __syncthreads();
       uint8_t* C = static_cast<uint8_t*>(args.C);
-      for (int c = tid; c < n_valid * 8; c += NT) {
-        const int trow = c / 8, ch = c % 8;
-        *reinterpret_cast<v4i*>(C + (size_t)(row0 + trow) * N + n0 + ch * 16) =
-            *reinterpret_cast<const v4i*>(ot + trow * 128 + ch * 16);
+      const int cpr = ncols * 2 / 16;              // 16-byte chunks per valid row
+      for (int c = tid; c < n_valid * cpr; c += NT) {
+        const int trow = c / cpr, ch = c % cpr;
+        *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) =
+            *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
+      }
+    } else {
+      // h = silu(gate) * up goes to LDS in fp32 (row stride 132 floats); then four
+      // threads per row take the row's 1x128 block: max |h|, the scale, the codes
+      constexpr int HS = 132;
+      float* hsm = reinterpret_cast<float*>(lds);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int trow = i * 16 + (lane >> 4) * 4 + r;
+          const int tcol = wid * WB + (lane & 15);
+          hsm[trow * HS + tcol] = silu_fast(acc[i][0][r]) * acc[i][1][r];
+        }
+      __syncthreads();
+      const int row = tid >> 2, part = tid & 3;
+      float hv[32];
+      float m = 0.f;
+      if (row < BM) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const v4f x = *reinterpret_cast<const v4f*>(hsm + row * HS + part * 32 + q * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hv[q * 4 + e] = x[e];
+            m = fmaxf(m, fabsf(x[e]));
+          }
+        }
+      }
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      if (row < n_valid) {
+        const float sc = block_scale(m);
+        const float inv = 1.0f / sc;
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          w[q] = e4m3x4(clamp448(hv[4 * q] * inv), clamp448(hv[4 * q + 1] * inv),
+                        clamp448(hv[4 * q + 2] * inv), clamp448(hv[4 * q + 3] * inv));
+        uint8_t* C = static_cast<uint8_t*>(args.C) + (size_t)(row0 + row) * N + n0 + part * 32;
+        *reinterpret_cast<v4i*>(C) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        *reinterpret_cast<v4i*>(C + 16) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+        if (part == 0) args.sC[(size_t)(row0 + row) * (N / 128) + n0 / 128] = sc;
       }
     }
-    __syncthreads();  // LDS (row_src, red, stages) is reused by the next tile
+    __syncthreads();  // LDS (row_src, table, stages) is reused by the next tile
   };
 
   for (int t = v; t < total; t += P) {
-    // ---- locate the tile
+    // ---- locate the tile: within a group, runs of up to GM row tiles are walked column
+    // tile by column tile
+    constexpr int GM = 8;
     const int g = find_group(tm, G, t, tiles_n);
     const int mt = tm.start[g + 1] - tm.start[g];
     const int local = t - tm.start[g] * tiles_n;
-    const int ni = local / mt, mi = local % mt;
-    const int rows = group_rows(tm, g), r0 = group_row0(tm, g);
-    const int n0 = ni * BN_OUT;
+    const int sr = local / (GM * tiles_n);
+    const int rows_sr = min(GM, mt - sr * GM);
+    const int idx = local - sr * GM * tiles_n;
+    const int mi = sr * GM + idx % rows_sr, ni = idx / rows_sr;
+    // tile coordinates are the same in every lane: scalar registers
+    const int gu = __builtin_amdgcn_readfirstlane(g);
+    const int rows = __builtin_amdgcn_readfirstlane(group_rows(tm, gu));
+    const int r0 = __builtin_amdgcn_readfirstlane(group_row0(tm, gu));
+    const int n0 = __builtin_amdgcn_readfirstlane(ni * BN_OUT);
+    const int miu = __builtin_amdgcn_readfirstlane(mi);
     if (rows <= BMS)
-      run_tile(std::integral_constant<int, BMS>{}, g, r0 + mi * BMS, r0 + rows, n0);
+      run_tile(std::integral_constant<int, BMS>{}, gu, r0 + miu * BMS, r0 + rows, n0);
     else
-      run_tile(std::integral_constant<int, BMB>{}, g, r0 + mi * BMB, r0 + rows, n0);
+      run_tile(std::integral_constant<int, BMB>{}, gu, r0 + miu * BMB, r0 + rows, n0);
   }
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows, int a_row_div,
-                           const uint8_t* B, const float* sB, const int32_t* offsets, int G,
+                           const uint8_t* Bf, const float* sB, const int32_t* offsets, int G,
                            int R_cap, int N, int K, bool swiglu, void* C, float* sC, int bm,
                            int num_cus, hipStream_t s, int rows_mode, int cap) {
-  GemmArgs a{A, sA, a_rows, a_row_div, B, sB, offsets, G, N, K, C, sC, rows_mode, cap};
-  const bool wide = !swiglu && N % 256 == 0;      // 256 output columns per plain tile
-  const long tiles_n = swiglu ? N / 128 : (wide ? N / 256 : N / 128);
+  if (K / 128 > kGemmMaxKBlocks) return hipErrorInvalidValue;
+  GemmArgs a{A, sA, a_rows, a_row_div, Bf, sB, offsets, G, N, K, C, sC, rows_mode, cap};
+  const long tiles_n = swiglu ? N / 128 : (N + 255) / 256;
   const long mtiles = R_cap / (bm < 128 ? bm : 64) + G;
   long grid = std::min<long>(mtiles * tiles_n, (long)num_cus);
   if (grid >= 8) grid = grid / 8 * 8;
   if (grid < 1) grid = 1;
   dim3 gd((unsigned)grid), bd(512);
-  // bm: tile rows of small groups (16, 32 or 64); groups above it use 128-row tiles
+  // bm: tile rows of small groups (16, 32 or 64); larger groups use 128-row tiles
   const int bms = bm >= 64 ? 64 : bm;
-#define MOE_GEMM_CASE(BMSV, BNBV, SW) \
-  hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, BNBV, SW>), gd, bd, 0, s, a)
+#define MOE_GEMM_CASE(BMSV, SW) hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, SW>), gd, bd, 0, s, a)
   if (swiglu) {
     switch (bms) {
-      case 16: MOE_GEMM_CASE(16, 256, true); break;
-      case 32: MOE_GEMM_CASE(32, 256, true); break;
-      case 64: MOE_GEMM_CASE(64, 256, true); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else if (wide) {
-    switch (bms) {
-      case 16: MOE_GEMM_CASE(16, 256, false); break;
-      case 32: MOE_GEMM_CASE(32, 256, false); break;
-      case 64: MOE_GEMM_CASE(64, 256, false); break;
+      case 16: MOE_GEMM_CASE(16, true); break;
+      case 32: MOE_GEMM_CASE(32, true); break;
+      case 64: MOE_GEMM_CASE(64, true); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (bms) {
-      case 16: MOE_GEMM_CASE(16, 128, false); break;
-      case 32: MOE_GEMM_CASE(32, 128, false); break;
-      case 64: MOE_GEMM_CASE(64, 128, false); break;
+      case 16: MOE_GEMM_CASE(16, false); break;
+      case 32: MOE_GEMM_CASE(32, false); break;
+      case 64: MOE_GEMM_CASE(64, false); break;
       default: return hipErrorInvalidValue;
     }
   }

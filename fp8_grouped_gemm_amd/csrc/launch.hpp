@@ -25,7 +25,13 @@ hipError_t launch_quant_weight_fp8(const float* w, int G, int N, int K, uint8_t*
                                    float* scales, hipStream_t s);
 hipError_t launch_quant_weight_int4(const float* w, int G, int N, int K, uint8_t* q, float* s7,
                                     hipStream_t s);
-// bm: rows per tile (16, 32, 64, 128; 128 only without SwiGLU)
+// The FP8 GEMM keeps a tile's activation scales for every K block in LDS: K <= 128 * this.
+constexpr int kGemmMaxKBlocks = 128;
+// B [G][R][K] e4m3 -> the fragment-major layout the FP8 GEMM reads (same byte count)
+hipError_t launch_pack_weight_fp8(const uint8_t* B, int G, int R, int K, uint8_t* Bf,
+                                  hipStream_t s);
+// bm: rows per tile of small groups (16, 32, 64; larger values mean 64); Bf is
+// fragment-major (launch_pack_weight_fp8)
 hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows,
                            int a_row_div, const uint8_t* B, const float* sB,
                            const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,

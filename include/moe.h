@@ -147,6 +147,15 @@ int moe_quant_fp8(const void *x, moe_dtype x_dt, int rows_in, int K, const int32
 int moe_quant_weight_fp8(const float *w, int G, int N, int K, uint8_t *q, float *scales,
                          void *stream);
 
+/* Rearranges e4m3 weight codes q [G, N, K] (as moe_quant_weight_fp8 writes them) into
+ * the fragment-major layout the FP8 GEMMs read: qf is [G][N/16][K/128][2][64][16 B],
+ * where half h, lane l of 16-row block nb and 128-deep block kb hold the 16 codes
+ * q[g][16 nb + (l mod 16)][128 kb + 32 (l div 16) + 16 h .. +16] -- the operand of one
+ * 16x16x128 matrix instruction in the order a wave loads it.  A pure permutation (same
+ * byte count, scales unchanged), done once per weight; q and qf must not overlap.
+ * N and K multiples of 128.  (Layout of this library, not of the pages.) */
+int moe_pack_weight_fp8(const uint8_t *q, int G, int N, int K, uint8_t *qf, void *stream);
+
 /* Block-wise int4 weights with 1x128 per-channel blocks (tqpw.cn sec. 3.1): for each
  * row n and 128-wide block, scale = max|w| (1 if 0), q = rne(fl32(fl32(w/scale)*7))
  * in [-7,7], s7 = fl32(scale/7).  w [G, N, K] fp32 -> q [G, N, K/2] packed as
@@ -161,12 +170,14 @@ int moe_quant_weight_int4(const float *w, int G, int N, int K, uint8_t *q, float
  * : r (a_rows[r] < 0: any row, output unspecified).  For each 128-deep K block kb
  * the e4m3 products are summed in fp32 and promoted as
  *   acc += sA[a, kb] * sB[g, n/128, kb] * partial.
- *   A [*, K] e4m3, sA [*, K/128] fp32; B [G, Nb, K] e4m3, sB [G, Nb/128, K/128] fp32
- *   with Nb = N (MOE_EPI_PLAIN) or 2N (MOE_EPI_SWIGLU).
+ *   A [*, K] e4m3, sA [*, K/128] fp32; B: the e4m3 codes of [G, Nb, K] weights in the
+ *   fragment-major layout of moe_pack_weight_fp8, sB [G, Nb/128, K/128] fp32, with
+ *   Nb = N (MOE_EPI_PLAIN) or 2N (MOE_EPI_SWIGLU).
  *   out_dt MOE_BF16: C [R_cap, N] bf16 (RNE), sC unused;
  *   out_dt MOE_E4M3 (SwiGLU only): C [R_cap, N] e4m3 codes of the fp32 SwiGLU output
  *     quantised 1x128 as moe_quant_fp8, sC [R_cap, N/128] fp32.
- * Rows >= offsets[G] and padding rows are unspecified.  N and K multiples of 128. */
+ * Rows >= offsets[G] and padding rows are unspecified.  N and K multiples of 128,
+ * K <= 16384 (the kernel keeps a tile's activation scales for all K blocks on chip). */
 int grouped_gemm_fp8(const uint8_t *A, const float *sA, const int32_t *a_rows, int a_row_div,
                      const uint8_t *B, const float *sB, const int32_t *offsets, int G,
                      int R_cap, int N, int K, int epilogue, moe_dtype out_dt, void *C,
@@ -184,9 +195,10 @@ int grouped_gemm_fp8_masked(const uint8_t *A, const float *sA, const uint8_t *B,
                             void *stream);
 
 /* Dense FP8 GEMM with the same block scaling (the dense layout, qidao123.com day 3):
- * C [M, N] bf16 = A [M, K] e4m3 (sA [M, K/128]) times B [N, K] e4m3 (sB [N/128, K/128])
- * transposed, promoted per 128-deep K block.  N and K multiples of 128, M >= 0 (M = 0:
- * nothing is launched, A, sA and C may be null). */
+ * C [M, N] bf16 = A [M, K] e4m3 (sA [M, K/128]) times B [N, K] e4m3 (sB [N/128, K/128],
+ * codes fragment-major as moe_pack_weight_fp8 with G = 1) transposed, promoted per
+ * 128-deep K block.  N and K multiples of 128, K <= 16384, M >= 0 (M = 0: nothing is
+ * launched, A, sA and C may be null). */
 int gemm_fp8(const uint8_t *A, const float *sA, const uint8_t *B, const float *sB, int M,
              int N, int K, uint16_t *C, void *stream);
 
@@ -224,10 +236,11 @@ typedef struct {
 typedef struct {
   const void *w_router;    /* [E, d]: bf16 (FP8/W4A16 modes) or fp32 (FP32 mode)    */
   const float *bias;       /* [E] fp32 (score routing)                              */
-  const void *w13;         /* [E, 2I, d]: rows [0,I) gate, [I,2I) up.  fp32 | e4m3 | */
-                           /*   int4 packed [E, 2I, d/2]                             */
+  const void *w13;         /* [E, 2I, d]: rows [0,I) gate, [I,2I) up.  fp32 | e4m3  */
+                           /*   fragment-major (moe_pack_weight_fp8) | int4 packed    */
+                           /*   [E, 2I, d/2]                                         */
   const float *s13;        /* FP8: [E, 2I/128, d/128]; W4A16: [E, 2I, d/128]        */
-  const void *w2;          /* [E, d, I] (int4: [E, d, I/2])                         */
+  const void *w2;          /* [E, d, I] (e4m3: fragment-major; int4: [E, d, I/2])   */
   const float *s2;         /* FP8: [E, d/128, I/128]; W4A16: [E, d, I/128]          */
 } moe_layer_weights;
 

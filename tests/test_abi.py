@@ -23,7 +23,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = _lib.load()
     declared = _declared()
-    assert len(declared) == 20, declared
+    assert len(declared) == 21, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -79,6 +79,10 @@ def test_dispatch_and_quant_reject_bad_args():
     _err(lib.moe_quant_fp8(FAKE, _lib.MOE_BF16, 4, 128, None, 1, 8, FAKE, FAKE, S), "rows_out")
     _err(lib.moe_quant_fp8(FAKE, _lib.MOE_INT4, 4, 128, None, 1, 4, FAKE, FAKE, S), "x_dt")
     _err(lib.moe_quant_weight_fp8(FAKE, 1, 100, 128, FAKE, FAKE, S), "multiples of 128")
+    _err(lib.moe_pack_weight_fp8(FAKE, 1, 128, 200, C.c_void_p(0x2000), S), "multiples of 128")
+    _err(lib.moe_pack_weight_fp8(FAKE, 1, 128, 128, FAKE, S), "overlap")
+    _err(lib.moe_pack_weight_fp8(None, 1, 128, 128, FAKE, S), "null")
+    _err(lib.gemm_fp8(FAKE, FAKE, FAKE, FAKE, 16, 128, 128 * 129, FAKE, S), "K must be <=")
     _err(lib.moe_quant_weight_int4(FAKE, 1, 8, 100, FAKE, FAKE, S), "K must")
 
 

@@ -54,6 +54,8 @@ def _layer_fullsize(w: synth.Workload, tokens):
     else:
         q13, s13 = M.moe_quant_weight_int4(inp["w13"])
         q2, s2 = M.moe_quant_weight_int4(inp["w2"])
+    if w.mode == "fp8":
+        q13, q2 = M.moe_pack_weight_fp8(q13), M.moe_pack_weight_fp8(q2)
     weights = {"w13": q13, "s13": s13, "w2": q2, "s2": s2}
     if w.route == "score":
         weights.update(w_router=inp["w_router"], bias=inp["bias"])
@@ -123,7 +125,8 @@ def test_fullsize_grouped_gemm_fp8():
     a[torch.from_numpy(dest).to(d)] = g["a"]
     qa, sa = M.moe_quant_fp8(a)
     qb, sb = M.moe_quant_weight_fp8(g["b"])
-    c = M.grouped_gemm_fp8(qa, sa, qb, sb, torch.from_numpy(offsets).to(d), R, N)
+    c = M.grouped_gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb), sb, torch.from_numpy(offsets).to(d),
+                           R, N)
     torch.cuda.synchronize()
     rows = np.concatenate([[offsets[i], offsets[i] + sizes[i] - 1] for i in range(16)])
     cblocks = [0, 17, 31]

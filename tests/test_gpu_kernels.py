@@ -84,6 +84,27 @@ def test_quant_weight_fp8_bitexact():
     np.testing.assert_array_equal(to_np(q), qo)
 
 
+def _pack_reference(q):
+    """The fragment-major layout written out with numpy: [G][N/16][K/128][2][64][16]
+    with half h, lane l of block (nb, kb) holding row 16 nb + l % 16, columns
+    128 kb + 32 (l // 16) + 16 h .. +16."""
+    G, N, K = q.shape
+    x = q.reshape(G, N // 16, 16, K // 128, 4, 2, 16)      # g, nb, r, kb, c, h, byte
+    x = x.transpose(0, 1, 3, 5, 4, 2, 6)                   # g, nb, kb, h, c, r, byte
+    return np.ascontiguousarray(x).reshape(G, N, K)        # lane = 16 c + r
+
+
+@pytest.mark.parametrize("shape", [(1, 128, 128), (3, 256, 384), (2, 384, 1024)])
+def test_pack_weight_fp8_permutation(shape):
+    note(f"pack weight fp8 {shape}")
+    q = torch.randint(0, 256, shape, dtype=torch.uint8, generator=torch.Generator().manual_seed(5))
+    qf = M.moe_pack_weight_fp8(q.to(dev()))
+    np.testing.assert_array_equal(to_np(qf), _pack_reference(q.numpy()))
+    # a [N, K] matrix packs as one group
+    q2 = M.moe_pack_weight_fp8(q[0].to(dev()))
+    np.testing.assert_array_equal(to_np(q2), _pack_reference(q[:1].numpy())[0])
+
+
 def test_quant_weight_int4_bitexact():
     note("quant weight int4")
     w = synth.normal((2, 40, 384), 8, "w2", std=0.02)
@@ -217,12 +238,13 @@ def test_grouped_gemm_fp8(sizes, m_align, swiglu):
     for g in range(len(sizes)):
         live[offsets[g]:offsets[g] + sizes[g]] = True
     if not swiglu:
-        c = M.grouped_gemm_fp8(qa, sa, qb, sb, off_d, R, N)
+        c = M.grouped_gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb), sb, off_d, R, N)
         beyond, raw = error_ratios(to_np(c)[live], ref[live])
         print(f"beyond={beyond:.3e} raw={raw:.3e}")
         assert beyond <= TOL
     else:
-        codes, sc = M.grouped_gemm_fp8(qa, sa, qb, sb, off_d, R, N, swiglu=True)
+        codes, sc = M.grouped_gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb), sb, off_d, R, N,
+                                       swiglu=True)
         A = OC.dequant_fp8_act(qao, sao)
         Bd = OC.dequant_fp8_weight(qbo, sbo)
         sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)      # sum_k |a_k b_k|
@@ -253,7 +275,8 @@ def test_grouped_gemm_fp8_row_gather():
     qx, sx = M.moe_quant_fp8(x.to(dev()))
     qw, sw = M.moe_quant_weight_fp8(w.to(dev()))
     R = len(sor)
-    c = M.grouped_gemm_fp8(qx, sx, qw, sw, torch.from_numpy(offsets).to(dev()), R, N,
+    c = M.grouped_gemm_fp8(qx, sx, M.moe_pack_weight_fp8(qw), sw,
+                           torch.from_numpy(offsets).to(dev()), R, N,
                            a_rows=torch.from_numpy(sor).to(dev()), a_row_div=k)
     qxo, sxo = OC.quant_fp8_act(x.float().numpy())
     qwo, swo = OC.quant_fp8_weight(w.numpy())
@@ -294,8 +317,8 @@ def test_grouped_gemm_fp8_masked(swiglu):
     qb, sb = M.moe_quant_weight_fp8(b.to(dev()))
     qao, sao = OC.quant_fp8_act(a.numpy())
     qbo, sbo = OC.quant_fp8_weight(b.numpy())
-    out = M.grouped_gemm_fp8_masked(qa, sa, qb, sb, torch.from_numpy(counts).to(dev()), cap, N,
-                                    swiglu=swiglu)
+    out = M.grouped_gemm_fp8_masked(qa, sa, M.moe_pack_weight_fp8(qb), sb,
+                                    torch.from_numpy(counts).to(dev()), cap, N, swiglu=swiglu)
     A = OC.dequant_fp8_act(qao, sao)
     Bd = OC.dequant_fp8_weight(qbo, sbo)
     for g in range(G):
@@ -323,7 +346,7 @@ def test_gemm_fp8_dense(Mrows):
         torch.empty((0, K), dtype=torch.uint8, device=dev()),
         torch.empty((0, K // 128), dtype=torch.float32, device=dev()))
     qb, sb = M.moe_quant_weight_fp8(b[None].to(dev()))
-    c = M.gemm_fp8(qa, sa, qb[0], sb[0])
+    c = M.gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb[0]), sb[0])
     assert tuple(c.shape) == (Mrows, N)
     if Mrows == 0:
         return
@@ -401,6 +424,7 @@ def test_determinism():
     a, b, offsets, R = _gemm_case([200, 3, 77], 256, 512, 16, 15, True)
     qa, sa = M.moe_quant_fp8(a.to(dev()))
     qb, sb = M.moe_quant_weight_fp8(b.to(dev()))
+    qb = M.moe_pack_weight_fp8(qb)
     off = torch.from_numpy(offsets).to(dev())
     c1, s1 = M.grouped_gemm_fp8(qa, sa, qb, sb, off, R, 256, swiglu=True)
     c2, s2 = M.grouped_gemm_fp8(qa, sa, qb, sb, off, R, 256, swiglu=True)

@@ -20,8 +20,9 @@ def _gpu_weights(w: synth.Workload, inp: dict) -> dict:
     if w.mode == "fp32":
         out["w13"], out["w2"] = inp["w13"].to(d), inp["w2"].to(d)
     elif w.mode == "fp8":
-        out["w13"], out["s13"] = M.moe_quant_weight_fp8(inp["w13"].to(d))
-        out["w2"], out["s2"] = M.moe_quant_weight_fp8(inp["w2"].to(d))
+        q13, out["s13"] = M.moe_quant_weight_fp8(inp["w13"].to(d))
+        q2, out["s2"] = M.moe_quant_weight_fp8(inp["w2"].to(d))
+        out["w13"], out["w2"] = M.moe_pack_weight_fp8(q13), M.moe_pack_weight_fp8(q2)
     else:
         out["w13"], out["s13"] = M.moe_quant_weight_int4(inp["w13"].to(d))
         out["w2"], out["s2"] = M.moe_quant_weight_int4(inp["w2"].to(d))
