@@ -68,6 +68,15 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_
                :: "s"(m), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
+// f(integral_constant<0>), ..., f(integral_constant<N-1>) in order
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
 // wait for this wave's LDS operations, then for the whole workgroup
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -115,7 +124,6 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
   constexpr int NW = 8, NT = 512, BMB = 128, TN = 2;
   constexpr int BN_OUT = SWIGLU ? 128 : 256;       // output columns per tile
   constexpr int WB = (SWIGLU ? 128 : 256) / NW;    // weight rows per wave (per half: SwiGLU)
-  constexpr int DB = 3;                            // weight ring: blocks kb .. kb+2
   constexpr int A_STAGE = BMB * 128;               // activation codes of one K block
   constexpr int NSA = 4;                           // activation stages
   constexpr int TAB_OFF = NSA * A_STAGE;           // row-scale table [kb][row]
@@ -146,6 +154,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
   auto run_tile = [&](auto BMC, int g, int row0, int row_end, int n0) {
     constexpr int BM = decltype(BMC)::value;
     constexpr int TM = BM / 16;                    // 16-row MFMA tiles per wave
+    // weight ring: blocks kb .. kb+DB-1.  Small tiles only stream weights, so they keep
+    // more blocks in flight (their accumulators are few).
+    constexpr int DB = BM <= 32 ? 6 : 3;
     const int n_valid = min(row_end - row0, BM);   // >= 1
     const int ncols = min(BN_OUT, N - n0);         // plain N % 256 == 128: half last tile
     if (tid < BM) {
@@ -210,6 +221,10 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     const float* sb1 = args.sB + ((size_t)g * RB + (SWIGLU ? (N + brow0) / 128 : 0)) * KB;
     constexpr int NB_OPS = 2 * TN + (SWIGLU ? 2 : 1);   // vector loads per load_b
 
+    // The barrier waits count this wave's vector memory operations (vmcnt), so every
+    // load_b must issue exactly NB_OPS of them: the compiler barrier at its end stops a
+    // clamped block's repeated addresses from being merged with the previous call's, and
+    // the never-taken sink after the K loop keeps the loads of blocks past the end alive.
     v8i bq[DB][TN];
     float sbq[DB][2];
     auto load_b = [&](int slot, int kb) {
@@ -223,6 +238,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
       }
       sbq[slot][0] = sb0[kb];
       sbq[slot][1] = SWIGLU ? sb1[kb] : 0.f;
+      asm volatile("" ::: "memory");
     };
 
     v4f acc[TM][TN];
@@ -236,10 +252,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     // AR sets; the reads of a block's last RA steps fetch the next block's first
     // fragments, published by the barrier RA steps before the block ends.  Promotion of
     // a step's partials runs one step behind its MFMAs (rings of PR), across blocks.
-    // Ring phases are compile-time because the K loop is unrolled by DB = 3 blocks.
+    // Ring phases are compile-time because the K loop is unrolled by DB blocks.
     constexpr int RA = TM < 2 ? TM : 2;
     constexpr int AR = 3;                          // divides DB * TM
     constexpr int PR = (TM % 2 == 0) ? 2 : 3;      // divides DB * TM
+    static_assert((DB * TM) % AR == 0 && (DB * TM) % PR == 0, "ring phases");
     v8i af[AR];
     v4f sa[AR];
     v4f pp[PR][TN];
@@ -322,11 +339,14 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     // prologue, in the steady-state order (weights of x, activations of x+1): block 0's
     // activations in LDS, weights of blocks 0 and 1 and activations of 1 and 2 in flight,
     // the first RA fragments of block 0 in registers
-    dma_a(0);
-    load_b(0, 0);
-    dma_a(1);
-    load_b(1, 1);
-    dma_a(2);
+    // (block kb issues the weights of kb+DB-1, then the activations of kb+3: replay that
+    // for the blocks before 0)
+    constexpr int KPRE = DB - 1 > 3 ? DB - 1 : 3;
+    static_for<KPRE>([&](auto T) {
+      constexpr int k = KPRE - decltype(T)::value;   // "block -k"
+      if constexpr (DB - 1 - k >= 0) load_b(DB - 1 - k, DB - 1 - k);
+      if constexpr (3 - k >= 0) dma_a(3 - k);
+    });
     wait_vmcnt<2 * NB_OPS + 2 * ADMA>();
     lds_barrier();
 #pragma unroll
@@ -342,13 +362,24 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
       for (int j = 0; j < TN; ++j) pp[p][j] = zero;
     }
     int kb = 0;
-    for (; kb + DB <= KB; kb += DB) {
-      body(std::integral_constant<int, 0>{}, kb);
-      body(std::integral_constant<int, 1>{}, kb + 1);
-      body(std::integral_constant<int, 2>{}, kb + 2);
+    for (; kb + DB <= KB; kb += DB)
+      static_for<DB>([&](auto U) { body(U, kb + decltype(U)::value); });
+    static_for<DB - 1>([&](auto U) {
+      if (kb + decltype(U)::value < KB) body(U, kb + decltype(U)::value);
+    });
+    if (G < 0) {
+      // never taken (G >= 1): uses every weight-ring slot, see load_b
+      int x = 0;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x ^= bq[d][j][e];
+        x ^= __float_as_int(sbq[d][0]) ^ __float_as_int(sbq[d][1]);
+      }
+      static_cast<int*>(args.C)[tid] = x;
     }
-    if (kb < KB) body(std::integral_constant<int, 0>{}, kb);
-    if (kb + 1 < KB) body(std::integral_constant<int, 1>{}, kb + 1);
     {
       // the last block's last step
       const int glast = ((KB - 1) % DB) * TM + TM - 1;
