@@ -336,10 +336,45 @@ def test_grouped_gemm_fp8_masked(swiglu):
             _check_swiglu_codes(to_np(out[0])[rows], to_np(out[1])[rows], ref, sab, N)
 
 
-@pytest.mark.parametrize("Mrows", [0, 1, 200, 333])
-def test_gemm_fp8_dense(Mrows):
-    N, K = 384, 512
-    note(f"gemm fp8 dense M={Mrows}")
+@pytest.mark.parametrize("K", [128, 256, 384, 640, 1536])
+@pytest.mark.parametrize("sizes,m_align", [
+    ([3, 20, 40, 150], 16),        # 32-row tiles (six-block weight ring) and 128-row tiles
+    ([1, 5, 9, 16, 2], 8),         # 16-row tiles
+])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_fp8_short_k(K, sizes, m_align, swiglu):
+    """K with fewer 128-deep blocks than the weight ring and the unrolled K loop: every
+    block count from 1 up, tails of every length."""
+    N = 128 if swiglu else 256
+    note(f"gemm fp8 short K={K} sizes={sizes} swiglu={swiglu}")
+    a, b, offsets, R = _gemm_case(sizes, N, K, m_align, 31, swiglu)
+    qa, sa = M.moe_quant_fp8(a.to(dev()))
+    qb, sb = M.moe_quant_weight_fp8(b.to(dev()))
+    qao, sao = OC.quant_fp8_act(a.numpy())
+    qbo, sbo = OC.quant_fp8_weight(b.numpy())
+    off_d = torch.from_numpy(offsets).to(dev())
+    ref = O.grouped_gemm_fp8(qao, sao, qbo, sbo, offsets)
+    live = np.zeros(R, bool)
+    for g in range(len(sizes)):
+        live[offsets[g]:offsets[g] + sizes[g]] = True
+    if not swiglu:
+        c = M.grouped_gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb), sb, off_d, R, N)
+        beyond, raw = error_ratios(to_np(c)[live], ref[live])
+        assert beyond <= TOL, beyond
+    else:
+        codes, sc = M.grouped_gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb), sb, off_d, R, N,
+                                       swiglu=True)
+        A = OC.dequant_fp8_act(qao, sao)
+        Bd = OC.dequant_fp8_weight(qbo, sbo)
+        sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)
+        _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
+
+
+@pytest.mark.parametrize("Mrows,K", [(0, 512), (1, 512), (200, 512), (333, 512),
+                                     (333, 128), (40, 256), (333, 640)])
+def test_gemm_fp8_dense(Mrows, K):
+    N = 384
+    note(f"gemm fp8 dense M={Mrows} K={K}")
     a = synth.normal((max(Mrows, 1), K), 22, "gemm_a")[:Mrows]
     b = synth.normal((N, K), 22, "gemm_b", std=K ** -0.5)
     qa, sa = M.moe_quant_fp8(a.to(dev())) if Mrows else (
