@@ -32,8 +32,10 @@
 //     tile, so that the K loop loads no scattered scale words.
 //   * Persistent grid; workgroup b works on tiles v, v+P, ... with v = (b mod 8) * P/8 +
 //     b/8, so that the 32 tiles one XCD holds at a time are consecutive; inside a group
-//     they run down up to 8 row tiles before moving to the next column tile, so those 32
-//     tiles share about 8 activation row tiles and 4 weight column tiles in that XCD's L2.
+//     they run down up to 8 row tiles before moving to the next column tile, so those
+//     tiles share a few activation row tiles and weight column tiles in that XCD's L2.
+//     The tiles of large groups (MFMA-bound) and of small groups (bound by the weight
+//     stream) are interleaved in proportion to their counts, so both kinds run at once.
 #include <algorithm>
 #include <type_traits>
 
@@ -61,12 +63,20 @@ struct GemmArgs {
   int mode, cap;  // GroupRows of the tile map and its C (masked) or M (dense)
 };
 
-// LDS DMA with a scalar base address and a 32-bit lane offset (see dma.hpp for why the
-// DMA is written as inline asm).
-__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t m) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(m), "v"(voff), "s"(sbase) : "memory", "m0");
+// Global->LDS DMA of 16 bytes per lane (lane L lands at lds_dst + 16 L) through a buffer
+// resource with a 32-bit lane offset.  Written with the compiler builtin, so the
+// compiler counts it among the vector memory operations (its waits for the weight
+// loads stay exact) and, as every activation stage is an LDS object of its own, tells
+// a DMA into one stage apart from reads of another.  (The flat-segment form of the
+// same builtin makes the compiler assume a pending LDS access and wait for zero.)
+__device__ __forceinline__ void dma16b(const void* base, uint32_t voff, void* lds_dst) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_dst,
+                                           16, voff, 0, 0, 0);
 }
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // f(integral_constant<0>), ..., f(integral_constant<N-1>) in order
 template <int N, typename F>
@@ -125,14 +135,25 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
   constexpr int BN_OUT = SWIGLU ? 128 : 256;       // output columns per tile
   constexpr int WB = (SWIGLU ? 128 : 256) / NW;    // weight rows per wave (per half: SwiGLU)
   constexpr int A_STAGE = BMB * 128;               // activation codes of one K block
-  constexpr int NSA = 4;                           // activation stages
-  constexpr int TAB_OFF = NSA * A_STAGE;           // row-scale table [kb][row]
-  constexpr int STAGE_BYTES = TAB_OFF + kGemmMaxKBlocks * BMB * 4;
-  constexpr int OUT_BYTES = SWIGLU ? BMB * 132 * 4 : BMB * 512;
-  constexpr int LDS_BYTES = STAGE_BYTES > OUT_BYTES ? STAGE_BYTES : OUT_BYTES;
+  constexpr int NSA = 4;                           // activation stage arrays
+  constexpr int TAB_FLOATS = kGemmMaxKBlocks * BMB;
+  constexpr int OUT_FLOATS = SWIGLU ? BMB * 132 : BMB * 128;
   __shared__ TileMap tm;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  // four activation stages, each an LDS object of its own (see dma16b); the row-scale
+  // table [kb][row] doubles as the epilogue's staging area
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[A_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[A_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[A_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[A_STAGE];
+  __shared__ __attribute__((aligned(1024))) float tab[TAB_FLOATS > OUT_FLOATS ? TAB_FLOATS : OUT_FLOATS];
   __shared__ int row_src[BMB];
+  auto stage = [&](auto S) -> uint8_t* {
+    constexpr int sidx = decltype(S)::value % NSA;
+    if constexpr (sidx == 0) return st0;
+    else if constexpr (sidx == 1) return st1;
+    else if constexpr (sidx == 2) return st2;
+    else return st3;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,14 +161,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
   const int tiles_n = (N + BN_OUT - 1) / BN_OUT;
   const int R = SWIGLU ? 2 * N : N;                // weight rows per group
   const int R16 = R / 16, RB = R / 128;
-  const uint32_t lds0 = lds_addr(lds);
   const int gsel = 2 * (lane >> 4);
   // 16-byte piece p of LDS row r sits in slot p ^ swz(r); pairs of 128-byte rows share a
   // 256-byte bank line, so the key changes every second row
   auto swz = [](int r) { return (r >> 1) & 7; };
 
-  build_tile_map<BMS, BMB, NT>(tm, args.offsets, G, args.mode, args.cap);
-  const int total = tm.start[G] * tiles_n;
+  build_tile_map<BMS, BMB, NT, true>(tm, args.offsets, G, args.mode, args.cap);
+  // large-group (128-row) and small-group tiles, interleaved in proportion to their
+  // counts, so that MFMA-bound and weight-streaming tiles share the machine at any time
+  const int n_big = tm.start[G] * tiles_n, n_small = tm.sstart[G] * tiles_n;
+  const int total = n_big + n_small;
   const int P = gridDim.x, b = blockIdx.x;
   const int v = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
 
@@ -157,6 +180,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     // weight ring: blocks kb .. kb+DB-1.  Small tiles only stream weights, so they keep
     // more blocks in flight (their accumulators are few).
     constexpr int DB = BM <= 32 ? 6 : 3;
+    constexpr int LEAD = NSA - 1;                  // activation DMA runs LEAD blocks ahead
+    static_assert(LEAD <= DB, "prologue order");
+    // the K loop is unrolled by UNR blocks, so that weight slots and activation stages
+    // are compile-time in every block
+    constexpr int UNR = DB * NSA / gcd_c(DB, NSA);
     const int n_valid = min(row_end - row0, BM);   // >= 1
     const int ncols = min(BN_OUT, N - n0);         // plain N % 256 == 128: half last tile
     if (tid < BM) {
@@ -185,17 +213,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
       a_voff[q] = (uint32_t)row_src[row] * (uint32_t)K + ((slot ^ swz(row)) << 4);
       a_m[q] = grp * 1024;
     }
-    auto dma_a = [&](int kb) {
-      const uint32_t st = lds0 + (uint32_t)(kb % NSA) * A_STAGE;
+    auto dma_a = [&](auto S, int kb) {
+      uint8_t* st = stage(S);
       const uint8_t* base = args.A + (size_t)min(kb, KB - 1) * 128;
 #pragma unroll
-      for (int q = 0; q < ADMA; ++q) dma16s(a_voff[q], base, st + a_m[q]);
+      for (int q = 0; q < ADMA; ++q) dma16b(base, a_voff[q], st + a_m[q]);
     };
 
     // ---- the tile's row scales, transposed into LDS [kb][row]: thread (row, q) fetches
     // blocks 4q .. 4q+3 of one row
     {
-      float* tab = reinterpret_cast<float*>(lds + TAB_OFF);
       const int nq = (KB + 3) / 4;
       for (int p = tid; p < BM * nq; p += NT) {
         const int row = p % BM, q = p / BM;
@@ -254,9 +281,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     // a step's partials runs one step behind its MFMAs (rings of PR), across blocks.
     // Ring phases are compile-time because the K loop is unrolled by DB blocks.
     constexpr int RA = TM < 2 ? TM : 2;
-    constexpr int AR = 3;                          // divides DB * TM
-    constexpr int PR = (TM % 2 == 0) ? 2 : 3;      // divides DB * TM
-    static_assert((DB * TM) % AR == 0 && (DB * TM) % PR == 0, "ring phases");
+    constexpr int AR = 3;                          // divides UNR * TM
+    constexpr int PR = (TM % 2 == 0) ? 2 : 3;      // divides UNR * TM
+    static_assert((UNR * TM) % AR == 0 && (UNR * TM) % PR == 0, "ring phases");
     v8i af[AR];
     v4f sa[AR];
     v4f pp[PR][TN];
@@ -269,8 +296,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
       return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
     auto rd_s = [&](int kbx, int i) {
-      return *reinterpret_cast<const v4f*>(lds + TAB_OFF +
-                                           (kbx * BMB + i * 16 + (lane >> 4) * 4) * 4);
+      return *reinterpret_cast<const v4f*>(tab + kbx * BMB + i * 16 + (lane >> 4) * 4);
     };
     auto promote = [&](int slot, int ii) {
 #pragma unroll
@@ -281,27 +307,28 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
       }
     };
 
-    // one K block.  Vector memory order per block: weights of block kb+2, then the
+    // one K block.  Vector memory order per block: weights of block kb+DB-1, then the
     // activation DMA of block kb+3 into the stage block kb-1 used (every wave finished
     // that stage before the previous block's barrier).
     auto body = [&](auto U, int kb) {
       constexpr int u = decltype(U)::value;
+      constexpr int ub = u % DB;
       constexpr int g0 = u * TM;                   // step index within the unrolled round
       load_b((u + DB - 1) % DB, kb + DB - 1);
       __builtin_amdgcn_sched_barrier(0);
-      dma_a(kb + 3);
+      dma_a(std::integral_constant<int, u + LEAD>{}, kb + LEAD);
       __builtin_amdgcn_sched_barrier(0);
-      const uint8_t* L = lds + (kb % NSA) * A_STAGE;
-      const uint8_t* Ln = lds + ((kb + 1) % NSA) * A_STAGE;
-      const float sbA = sbq[u][0], sbB = SWIGLU ? sbq[u][1] : sbq[u][0];
+      const uint8_t* L = stage(U);
+      const uint8_t* Ln = stage(std::integral_constant<int, u + 1>{});
+      const float sbA = sbq[ub][0], sbB = SWIGLU ? sbq[ub][1] : sbq[ub][0];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int gs = g0 + i;
         if (i == TM - RA) {
           // this wave's DMA of block kb+1 (issued two blocks ago) has landed: after it
-          // came the weights of kb+1 and kb+2 and the DMAs of kb+2 and kb+3.  The barrier
-          // publishes block kb+1; every wave's reads of stage kb%NSA before it are done.
-          wait_vmcnt<2 * NB_OPS + 2 * ADMA>();
+          // came the two later blocks' weight loads and DMAs.  The barrier publishes
+          // block kb+1; every wave's reads of stage kb%NSA before it are done.
+          wait_vmcnt<(LEAD - 1) * (NB_OPS + ADMA)>();
           lds_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -319,11 +346,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           pp[gs % PR][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[gs % AR], bq[u][j], zero, 0, 0, 0, 0, 0, 0);
+              af[gs % AR], bq[ub][j], zero, 0, 0, 0, 0, 0, 0);
         cq[gs % PR][0] = sa[gs % AR] * sbA;
         cq[gs % PR][1] = sa[gs % AR] * sbB;
         // the previous step's partials (before the tile's first block: zeros)
-        promote((gs + DB * TM - 1) % PR, i > 0 ? i - 1 : TM - 1);
+        promote((gs + UNR * TM - 1) % PR, i > 0 ? i - 1 : TM - 1);
         // issue order inside a step: next fragment's reads, then each MFMA followed by
         // four promotion FMAs that run in its shadow; nothing moves across steps
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
@@ -336,22 +363,21 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
       }
     };
 
-    // prologue, in the steady-state order (weights of x, activations of x+1): block 0's
-    // activations in LDS, weights of blocks 0 and 1 and activations of 1 and 2 in flight,
-    // the first RA fragments of block 0 in registers
-    // (block kb issues the weights of kb+DB-1, then the activations of kb+3: replay that
-    // for the blocks before 0)
-    constexpr int KPRE = DB - 1 > 3 ? DB - 1 : 3;
+    // prologue: block 0's activations in LDS, the weights of blocks 0 .. DB-2 and the
+    // activations of blocks 1 and 2 in flight, the first RA fragments of block 0 in
+    // registers (block kb issues the weights of kb+DB-1, then the activations of kb+3:
+    // replayed for the blocks before 0, so the vector memory order is the steady one)
+    constexpr int KPRE = DB - 1 > LEAD ? DB - 1 : LEAD;
     static_for<KPRE>([&](auto T) {
       constexpr int k = KPRE - decltype(T)::value;   // "block -k"
       if constexpr (DB - 1 - k >= 0) load_b(DB - 1 - k, DB - 1 - k);
-      if constexpr (3 - k >= 0) dma_a(3 - k);
+      if constexpr (LEAD - k >= 0) dma_a(std::integral_constant<int, LEAD - k>{}, LEAD - k);
     });
-    wait_vmcnt<2 * NB_OPS + 2 * ADMA>();
+    wait_vmcnt<(LEAD - 1) * (NB_OPS + ADMA)>();
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
-      af[i] = rd_a(lds, i);
+      af[i] = rd_a(stage(std::integral_constant<int, 0>{}), i);
       sa[i] = rd_s(0, i);
     }
 #pragma unroll
@@ -362,9 +388,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
       for (int j = 0; j < TN; ++j) pp[p][j] = zero;
     }
     int kb = 0;
-    for (; kb + DB <= KB; kb += DB)
-      static_for<DB>([&](auto U) { body(U, kb + decltype(U)::value); });
-    static_for<DB - 1>([&](auto U) {
+    for (; kb + UNR <= KB; kb += UNR)
+      static_for<UNR>([&](auto U) { body(U, kb + decltype(U)::value); });
+    static_for<UNR - 1>([&](auto U) {
       if (kb + decltype(U)::value < KB) body(U, kb + decltype(U)::value);
     });
     if (G < 0) {
@@ -382,7 +408,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     }
     {
       // the last block's last step
-      const int glast = ((KB - 1) % DB) * TM + TM - 1;
+      const int glast = ((KB - 1) % UNR) * TM + TM - 1;
       if (glast % PR == 0) promote(0, TM - 1);
       else if (glast % PR == 1) promote(1, TM - 1);
       else if constexpr (PR > 2) promote(2, TM - 1);
@@ -394,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     if constexpr (!SWIGLU) {
       // bf16 tile staged through LDS for 16-byte stores
       constexpr int OB = 512;
-      uint8_t* ot = lds;
+      uint8_t* ot = reinterpret_cast<uint8_t*>(tab);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -418,7 +444,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
       // h = silu(gate) * up goes to LDS in fp32 (row stride 132 floats); then four
       // threads per row take the row's 1x128 block: max |h|, the scale, the codes
       constexpr int HS = 132;
-      float* hsm = reinterpret_cast<float*>(lds);
+      float* hsm = tab;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -465,9 +491,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     // ---- locate the tile: within a group, runs of up to GM row tiles are walked column
     // tile by column tile
     constexpr int GM = 8;
-    const int g = find_group(tm, G, t, tiles_n);
-    const int mt = tm.start[g + 1] - tm.start[g];
-    const int local = t - tm.start[g] * tiles_n;
+    // tile t is the a0-th large-group tile if floor(t n_big / total) steps at t,
+    // else the (t - a0)-th small-group tile
+    const int a0 = (int)((long long)t * n_big / total);
+    const int a1 = (int)((long long)(t + 1) * n_big / total);
+    const bool big = a1 > a0;
+    const int j = big ? a0 : t - a0;
+    const int* st = big ? tm.start : tm.sstart;
+    const int g = find_group(st, G, j, tiles_n);
+    const int mt = st[g + 1] - st[g];
+    const int local = j - st[g] * tiles_n;
     const int sr = local / (GM * tiles_n);
     const int rows_sr = min(GM, mt - sr * GM);
     const int idx = local - sr * GM * tiles_n;
@@ -520,3 +553,4 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_r
 }
 
 }  // namespace moe
+

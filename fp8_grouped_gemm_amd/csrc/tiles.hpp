@@ -4,10 +4,10 @@
 // offsets [offsets[g], offsets[g+1]); fixed-capacity ("masked"), rows [g C, g C +
 // counts[g]) of a [G, C] row block per group; dense, a single group of M rows.  Each
 // group is cut into ceil(M_g / BM) row tiles and every row tile into tiles_n column
-// tiles.  Tiles are numbered group
-// by group, column tile by column tile, row tile fastest, so that consecutive tiles
-// share one B column tile (a flattened tile list over all groups, as the global tile
-// scheduler in the MegaMoE walkthrough, discosf.com sec. 3.2, describes).
+// tiles.  Tiles are numbered group by group (a flattened tile list over all groups, as
+// the global tile scheduler in the MegaMoE walkthrough, discosf.com sec. 3.2,
+// describes).  A split map keeps two such lists: the large groups' row tiles (start)
+// and the small groups' single row tiles (sstart), for kernels that interleave them.
 #pragma once
 #include "common.hpp"
 
@@ -21,6 +21,7 @@ enum GroupRows { kRowsOffsets = 0, kRowsMasked = 1, kRowsDense = 2 };
 // Tile bookkeeping shared by the workgroup: per-group row-tile prefix sums.
 struct TileMap {
   int start[kMaxGroups + 1];  // first row tile of each group (exclusive prefix)
+  int sstart[kMaxGroups + 1]; // split maps: first small-group tile (start: large groups)
   int off[kMaxGroups + 1];    // offsets: copy; masked: counts clamped to [0, C]; dense: 0, M
   int mode, cap;              // GroupRows and C (masked) or M (dense)
 };
@@ -37,12 +38,12 @@ __device__ __forceinline__ int group_rows(const TileMap& tm, int g) {
 template <int BMS, int BMB>
 __device__ __forceinline__ int tile_rows(int M) { return M <= BMS ? BMS : BMB; }
 
-template <int BMS, int BMB = BMS, int NT = 256>
+template <int BMS, int BMB = BMS, int NT = 256, bool SPLIT = false>
 __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int G,
                                int mode = kRowsOffsets, int cap = 0) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  __shared__ int wsum[NW];
+  __shared__ int wsum[NW], wsum2[NW];
   if (tid == 0) {
     tm.mode = mode;
     tm.cap = cap;
@@ -56,41 +57,72 @@ __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets,
   // each thread owns a contiguous chunk of groups
   const int per = (G + NT - 1) / NT;
   const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
-  int local = 0;
-  for (int g = g0; g < g1; ++g) {
+  // row tiles of group g: all of them (combined map) or, for a split map, the large
+  // groups' (first) and the small groups' (second)
+  auto count = [&](int g, int& big, int& small) {
     const int M = group_rows(tm, g);
-    const int bm = tile_rows<BMS, BMB>(M);
-    local += (M + bm - 1) / bm;
+    if (SPLIT) {
+      big = M > BMS ? (M + BMB - 1) / BMB : 0;
+      small = (M > 0 && M <= BMS) ? 1 : 0;
+    } else {
+      const int bm = tile_rows<BMS, BMB>(M);
+      big = (M + bm - 1) / bm;
+      small = 0;
+    }
+  };
+  int local = 0, local2 = 0;
+  for (int g = g0; g < g1; ++g) {
+    int b, s;
+    count(g, b, s);
+    local += b;
+    local2 += s;
   }
-  int incl = local;
+  int incl = local, incl2 = local2;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
+    int v = __shfl_up(incl, o, 64), v2 = __shfl_up(incl2, o, 64);
+    if (lane >= o) {
+      incl += v;
+      incl2 += v2;
+    }
   }
-  if (lane == 63) wsum[wid] = incl;
+  if (lane == 63) {
+    wsum[wid] = incl;
+    wsum2[wid] = incl2;
+  }
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wid; ++w) base += wsum[w];
-  int run = base + incl - local;
+  int base = 0, base2 = 0;
+  for (int w = 0; w < wid; ++w) {
+    base += wsum[w];
+    base2 += wsum2[w];
+  }
+  int run = base + incl - local, run2 = base2 + incl2 - local2;
   for (int g = g0; g < g1; ++g) {
     tm.start[g] = run;
-    const int M = group_rows(tm, g);
-    const int bm = tile_rows<BMS, BMB>(M);
-    run += (M + bm - 1) / bm;
+    if (SPLIT) tm.sstart[g] = run2;
+    int b, s;
+    count(g, b, s);
+    run += b;
+    run2 += s;
   }
-  if (tid == NT - 1) tm.start[G] = base + incl;
+  if (tid == NT - 1) {
+    tm.start[G] = base + incl;
+    if (SPLIT) tm.sstart[G] = base2 + incl2;
+  }
   __syncthreads();
 }
 
 // largest g in [0, G) with start[g] * tiles_n <= t
-__device__ __forceinline__ int find_group(const TileMap& tm, int G, int t, int tiles_n) {
+__device__ __forceinline__ int find_group(const int* start, int G, int t, int tiles_n) {
   int lo = 0, hi = G - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if (tm.start[mid] * tiles_n <= t) lo = mid; else hi = mid - 1;
+    if (start[mid] * tiles_n <= t) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+__device__ __forceinline__ int find_group(const TileMap& tm, int G, int t, int tiles_n) {
+  return find_group(tm.start, G, t, tiles_n);
 }
 
 }  // namespace moe
