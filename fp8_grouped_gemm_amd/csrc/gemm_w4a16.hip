@@ -109,6 +109,12 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;       // 32x32x16 MFMA operand: row l32, k half hf
+  // XOR keys of the 16-byte pieces of an A row (256 B) and of a code row (64 B).  The LDS
+  // (64 four-byte banks) serves a 16-byte read for lanes {0-7, 16-23}, {8-15, 24-31},
+  // {32-39, 48-55}, {40-47, 56-63} together; those 16 lanes read rows r..r+7 and
+  // r+16..r+23 at one piece index, and the keys send them to 16 different bank groups.
+  auto akey = [](int row) { return (row & 7) | ((row >> 1) & 8); };
+  auto ckey = [](int r) { return ((r >> 2) & 1) | ((r >> 3) & 2); };
   const int G = args.G, K = args.K, N = args.N, KB = K / 128;
   const int NBtot = SWIGLU ? 2 * N : N;
   const int tiles_n = (N + BNO - 1) / BNO;
@@ -134,23 +140,25 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
     const bool wactive = SWIGLU || wid * 64 < ncols;  // else: repeated rows, not stored
 
     // A: an instruction fills 4 rows of 256 B; lane L lands at row L/16, slot L%16 and
-    // fetches 16-byte piece (L%16) ^ (row%16), the XOR swizzle read back below.
+    // fetches 16-byte piece (L%16) ^ akey(row), the XOR swizzle read back below.
     const uint8_t* a_src[A_IN];
 #pragma unroll
     for (int i = 0; i < A_IN; ++i) {
       const int row = (wid * A_IN + i) * 4 + (lane >> 4);
       a_src[i] = reinterpret_cast<const uint8_t*>(args.A + (size_t)row_src[row] * K) +
-                 (((lane & 15) ^ (row & 15)) << 4);
+                 (((lane & 15) ^ akey(row)) << 4);
     }
     const int a_cnt = min(max((n_valid - wid * A_IN * 4 + 3) / 4, 0), A_IN);
     const int per = a_cnt + B_IN + 1;
-    // codes: an instruction fills 16 weight rows of 64 B (row L/4, piece L%4); every
-    // wave fetches its own 64 rows and their 64 scales
+    // codes: an instruction fills 16 weight rows of 64 B (row L/4, slot L%4, holding
+    // piece (L%4) ^ ckey(row)); every wave fetches its own 64 rows and their 64 scales
     const uint8_t* b_src[B_IN];
 #pragma unroll
-    for (int i = 0; i < B_IN; ++i)
-      b_src[i] = args.B + ((size_t)g * NBtot + wrow(wid * 64 + i * 16 + (lane >> 2), n0)) *
-                              (K / 2) + (lane & 3) * 16;
+    for (int i = 0; i < B_IN; ++i) {
+      const int r = wid * 64 + i * 16 + (lane >> 2);
+      b_src[i] = args.B + ((size_t)g * NBtot + wrow(r, n0)) * (K / 2) +
+                 (((lane & 3) ^ ckey(r)) << 4);
+    }
     const float* s_src = args.s7 + ((size_t)g * NBtot + wrow(wid * 64 + lane, n0)) * KB;
     const uint32_t m_a = lds0 + (uint32_t)wid * (A_IN * 1024);
     const uint32_t m_b = lds0 + BR_OFF + (uint32_t)wid * (B_IN * 1024);
@@ -190,9 +198,9 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = wid * 64 + j * 32 + l32;
-        const uint8_t* src = L + BR_OFF + r * 64 + hf * 32;
-        raw[j][0] = *reinterpret_cast<const v4i*>(src);
-        raw[j][1] = *reinterpret_cast<const v4i*>(src + 16);
+        const uint8_t* src = L + BR_OFF + r * 64;
+        raw[j][0] = *reinterpret_cast<const v4i*>(src + (((2 * hf) ^ ckey(r)) << 4));
+        raw[j][1] = *reinterpret_cast<const v4i*>(src + (((2 * hf + 1) ^ ckey(r)) << 4));
         tab[j] = make_tab(reinterpret_cast<const float*>(L + SC_OFF)[r]);
       }
       auto expand_step = [&](int kk, v8bf* bf) {
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
         for (int i = 0; i < TM; ++i) {
           const int row = i * 32 + l32;
           af[i] = *reinterpret_cast<const v8bf*>(L + row * ROWB +
-                                                 (((8 * hf + kk) ^ (row & 15)) << 4));
+                                                 (((8 * hf + kk) ^ akey(row)) << 4));
         }
       };
       // software pipeline over the 8 steps: while the TM x TN MFMAs of step kk run, the
