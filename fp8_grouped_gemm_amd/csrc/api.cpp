@@ -101,6 +101,24 @@ int v_dispatch(const void* idx, int T, int k, int E, int m_align, int cap, const
   return MOE_OK;
 }
 
+// true if the byte ranges [a, a + na) and [b, b + nb) share a byte
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return a && b && na && nb && x < y + nb && y < x + na;
+}
+
+// The FP8 GEMM reads the weight scales through the scalar cache, which a store of the
+// same launch would not update: its outputs must not overlap them.
+int v_fp8_out_vs_scales(const char* fn, const float* sB, int G, int Nb, int K, const void* C,
+                        const float* sC, long long rows, int N, bool swiglu) {
+  const size_t nsb = (size_t)G * (Nb / 128) * (K / 128) * sizeof(float);
+  const size_t nc = (size_t)rows * N * (swiglu ? 1 : 2);
+  const size_t nsc = swiglu ? (size_t)rows * (N / 128) * sizeof(float) : 0;
+  REQUIRE(!overlaps(sB, nsb, C, nc) && !overlaps(sB, nsb, sC, nsc),
+          "%s: C and sC must not overlap sB", fn);
+  return MOE_OK;
+}
+
 int v_gemm_common(const void* A, const void* B, const void* offsets, int G, int R_cap, int N,
                   int K, int epilogue, const void* C) {
   REQUIRE(A && B && offsets && C, "grouped GEMM: null pointer");
@@ -268,6 +286,9 @@ int grouped_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows, i
   } else {
     REQUIRE(out_dt == MOE_BF16, "grouped_gemm_fp8: plain epilogue writes bf16");
   }
+  if ((st = v_fp8_out_vs_scales("grouped_gemm_fp8", sB, G, swiglu ? 2 * N : N, K, C, sC, R_cap,
+                                N, swiglu)))
+    return st;
   if (R_cap == 0) return MOE_OK;
   int cus = 0;
   if ((st = current_device(&cus))) return st;
@@ -296,6 +317,9 @@ int grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B,
   } else {
     REQUIRE(out_dt == MOE_BF16, "grouped_gemm_fp8_masked: plain epilogue writes bf16");
   }
+  if ((st = v_fp8_out_vs_scales("grouped_gemm_fp8_masked", sB, G, swiglu ? 2 * N : N, K, C, sC,
+                                rows, N, swiglu)))
+    return st;
   if (rows == 0) return MOE_OK;
   int cus = 0;
   if ((st = current_device(&cus))) return st;
@@ -312,9 +336,11 @@ int gemm_fp8(const uint8_t* A, const float* sA, const uint8_t* B, const float* s
   REQUIRE(N % 128 == 0 && K % 128 == 0, "gemm_fp8: N and K must be multiples of 128");
   REQUIRE(K / 128 <= moe::kGemmMaxKBlocks, "gemm_fp8: K must be <= %d",
           128 * moe::kGemmMaxKBlocks);
+  int st = v_fp8_out_vs_scales("gemm_fp8", sB, 1, N, K, C, nullptr, M, N, false);
+  if (st) return st;
   if (M == 0) return MOE_OK;
   int cus = 0;
-  int st = current_device(&cus);
+  st = current_device(&cus);
   if (st) return st;
   return hip_status(moe::launch_gemm_fp8(A, sA, nullptr, 1, B, sB, nullptr, 1, M, N, K, false, C,
                                          nullptr, pick_bm(M, false), cus, S(stream),

@@ -53,7 +53,6 @@ struct GemmArgs {
   const int32_t* a_rows;
   int a_row_div;
   const uint8_t* Bf;  // fragment-major weights
-  const float* sB;
   const int32_t* offsets;
   int G;
   int N;  // output columns
@@ -129,8 +128,12 @@ hipError_t launch_pack_weight_fp8(const uint8_t* B, int G, int R, int K, uint8_t
 
 // Two tile classes share one persistent tile list: groups with at most BMS rows get
 // BMS-row tiles (their cost is the weight stream), larger groups 128-row tiles.
+// The weight scales come as a separate restrict argument: the compiler can then prove
+// that no store of the kernel changes them and fetch them with scalar loads (one per
+// wave and K block, off the vector memory path).
 template <int BMS, bool SWIGLU>
-__global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
+__global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
+                                                           const float* __restrict__ sB) {
   constexpr int NW = 8, NT = 512, BMB = 128, TN = 2;
   constexpr int BN_OUT = SWIGLU ? 128 : 256;       // output columns per tile
   constexpr int WB = (SWIGLU ? 128 : 256) / NW;    // weight rows per wave (per half: SwiGLU)
@@ -251,9 +254,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args) {
     // plain: fragment j is block j; SwiGLU: j = 0 gate, j = 1 the up row N further on
     const size_t b_next = SWIGLU ? (size_t)(N / 16) * b_step : b_step;
     const uint32_t b_lane = lane * 16;
-    const float* sb0 = args.sB + ((size_t)g * RB + brow0 / 128) * KB;
-    const float* sb1 = args.sB + ((size_t)g * RB + (SWIGLU ? (N + brow0) / 128 : 0)) * KB;
-    constexpr int NB_OPS = 2 * TN + (SWIGLU ? 2 : 1);   // vector loads per load_b
+    const float* sb0 = sB + ((size_t)g * RB + brow0 / 128) * KB;
+    const float* sb1 = sB + ((size_t)g * RB + (SWIGLU ? (N + brow0) / 128 : 0)) * KB;
+    constexpr int NB_OPS = 2 * TN;                 // vector loads per load_b
 
     // The barrier waits count this wave's vector memory operations (vmcnt), so every
     // load_b must issue exactly NB_OPS of them: the compiler barrier at its end stops a
@@ -530,7 +533,7 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_r
                            int R_cap, int N, int K, bool swiglu, void* C, float* sC, int bm,
                            int num_cus, hipStream_t s, int rows_mode, int cap) {
   if (K / 128 > kGemmMaxKBlocks) return hipErrorInvalidValue;
-  GemmArgs a{A, sA, a_rows, a_row_div, Bf, sB, offsets, G, N, K, C, sC, rows_mode, cap};
+  GemmArgs a{A, sA, a_rows, a_row_div, Bf, offsets, G, N, K, C, sC, rows_mode, cap};
   const long tiles_n = swiglu ? N / 128 : (N + 255) / 256;
   const long mtiles = R_cap / (bm < 128 ? bm : 64) + G;
   long grid = std::min<long>(mtiles * tiles_n, (long)num_cus);
@@ -539,7 +542,7 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_r
   dim3 gd((unsigned)grid), bd(512);
   // bm: tile rows of small groups (16, 32 or 64); larger groups use 128-row tiles
   const int bms = bm >= 64 ? 64 : bm;
-#define MOE_GEMM_CASE(BMSV, SW) hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, SW>), gd, bd, 0, s, a)
+#define MOE_GEMM_CASE(BMSV, SW) hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, SW>), gd, bd, 0, s, a, sB)
   if (swiglu) {
     switch (bms) {
       case 16: MOE_GEMM_CASE(16, true); break;

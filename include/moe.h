@@ -177,7 +177,9 @@ int moe_quant_weight_int4(const float *w, int G, int N, int K, uint8_t *q, float
  *   out_dt MOE_E4M3 (SwiGLU only): C [R_cap, N] e4m3 codes of the fp32 SwiGLU output
  *     quantised 1x128 as moe_quant_fp8, sC [R_cap, N/128] fp32.
  * Rows >= offsets[G] and padding rows are unspecified.  N and K multiples of 128,
- * K <= 16384 (the kernel keeps a tile's activation scales for all K blocks on chip). */
+ * K <= 16384 (the kernel keeps a tile's activation scales for all K blocks on chip).
+ * C and sC must not overlap sB (checked: the kernel reads sB through the scalar cache)
+ * nor any other input (not checked). */
 int grouped_gemm_fp8(const uint8_t *A, const float *sA, const int32_t *a_rows, int a_row_div,
                      const uint8_t *B, const float *sB, const int32_t *offsets, int G,
                      int R_cap, int N, int K, int epilogue, moe_dtype out_dt, void *C,
@@ -198,7 +200,7 @@ int grouped_gemm_fp8_masked(const uint8_t *A, const float *sA, const uint8_t *B,
  * C [M, N] bf16 = A [M, K] e4m3 (sA [M, K/128]) times B [N, K] e4m3 (sB [N/128, K/128],
  * codes fragment-major as moe_pack_weight_fp8 with G = 1) transposed, promoted per
  * 128-deep K block.  N and K multiples of 128, K <= 16384, M >= 0 (M = 0: nothing is
- * launched, A, sA and C may be null). */
+ * launched, A, sA and C may be null).  C must not overlap sB (checked) nor A, sA, B. */
 int gemm_fp8(const uint8_t *A, const float *sA, const uint8_t *B, const float *sB, int M,
              int N, int K, uint16_t *C, void *stream);
 

@@ -104,6 +104,16 @@ def test_gemm_and_combine_reject_bad_args():
     _err(lib.grouped_gemm_fp8_masked(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 128, 100, 0,
                                      _lib.MOE_BF16, FAKE, None, S), "multiples of 128")
     _err(lib.gemm_fp8(FAKE, FAKE, FAKE, FAKE, 16, 384, 200, FAKE, S), "multiples of 128")
+    # outputs overlapping the weight scales (read through the scalar cache)
+    base = 0x100000
+    _err(lib.gemm_fp8(FAKE, FAKE, FAKE, C.c_void_p(base), 16, 256, 256,
+                      C.c_void_p(base + 8), S), "must not overlap sB")
+    _err(lib.grouped_gemm_fp8(FAKE, FAKE, None, 1, FAKE, C.c_void_p(base), FAKE, 2, 64, 128, 256,
+                              1, _lib.MOE_E4M3, FAKE, C.c_void_p(base + 16), S),
+         "must not overlap sB")
+    _err(lib.grouped_gemm_fp8_masked(FAKE, FAKE, FAKE, C.c_void_p(base), FAKE, 2, 16, 128, 128,
+                                     0, _lib.MOE_BF16, C.c_void_p(base - 64), None, S),
+         "must not overlap sB")
     _err(lib.gemm_fp8(None, FAKE, FAKE, FAKE, 16, 128, 128, FAKE, S), "null")
     _err(lib.grouped_gemm_w4a16(FAKE, None, 1, FAKE, FAKE, FAKE, 2, 64, 96, 128, 1, FAKE, S),
          "multiple of 128")
