@@ -1,6 +1,7 @@
 // Device-side helpers shared by the gfx950 kernels: vector types, bf16 / e4m3
 // conversions and wave64 reductions.
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -69,6 +70,17 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // GEMM epilogues whose result is rounded to 8 bits right after.
 __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
+// f(integral_constant<0>), ..., f(integral_constant<N-1>) in order
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
 }
 
 }  // namespace moe

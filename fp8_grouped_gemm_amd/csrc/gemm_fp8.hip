@@ -62,30 +62,6 @@ struct GemmArgs {
   int mode, cap;  // GroupRows of the tile map and its C (masked) or M (dense)
 };
 
-// Global->LDS DMA of 16 bytes per lane (lane L lands at lds_dst + 16 L) through a buffer
-// resource with a 32-bit lane offset.  Written with the compiler builtin, so the
-// compiler counts it among the vector memory operations (its waits for the weight
-// loads stay exact) and, as every activation stage is an LDS object of its own, tells
-// a DMA into one stage apart from reads of another.  (The flat-segment form of the
-// same builtin makes the compiler assume a pending LDS access and wait for zero.)
-__device__ __forceinline__ void dma16b(const void* base, uint32_t voff, void* lds_dst) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_dst,
-                                           16, voff, 0, 0, 0);
-}
-
-constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
-
-// f(integral_constant<0>), ..., f(integral_constant<N-1>) in order
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (N > 0) {
-    static_for<N - 1>(f);
-    f(std::integral_constant<int, N - 1>{});
-  }
-}
-
 // wait for this wave's LDS operations, then for the whole workgroup
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");

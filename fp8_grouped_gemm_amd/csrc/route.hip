@@ -6,98 +6,140 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
 // ---------------------------------------------------------------- router GEMM
 // logits[T, E] = x[T, d] . W[E, d]^T with bf16 inputs and fp32 accumulation on the
-// 16x16x32 bf16 MFMA.  Workgroup tile 64 tokens x 64 experts, 4 waves as 2x2 of
-// 32x32; K staged through LDS in 128-wide chunks, two chunks in flight in registers.
+// 16x16x32 bf16 MFMA.  Workgroup tile 128 tokens x 256 experts, 8 waves as 2 x 4 wave
+// tiles of 64 x 64.  64-deep K chunks of both operands reach LDS by DMA into three
+// stages (separate LDS objects), two chunks ahead, one barrier per chunk.  With split-K
+// every workgroup sums its range of chunks into partial plane blockIdx.z; the top-k
+// kernel adds the planes in plane order.
 namespace {
-constexpr int RT_BM = 64, RT_BN = 64, RT_BK = 128;      // BK in elements
-constexpr int RT_ROWB = RT_BK * 2;                        // 256 bytes per row per chunk
-constexpr int RT_CPR = RT_ROWB / 16;                      // 16-byte pieces per row: 16
-constexpr int RT_LOADS = RT_BM * RT_CPR / 256;            // per thread per operand: 4
+constexpr int RT_BM = 128, RT_BN = 256, RT_BK = 64;   // BK in elements: 128-byte rows
+constexpr int RT_SA = RT_BM * 128, RT_SB = RT_BN * 128;   // stage bytes per operand
+constexpr int RT_ADMA = RT_BM / 8 / 8, RT_BDMA = RT_BN / 8 / 8;   // DMAs per wave per chunk
+constexpr int RT_MIN_CHUNKS = 4;                      // per workgroup under split-K
+
+// XOR key of the 16-byte pieces of a 128-byte LDS row.  A fragment read hands the 16
+// lanes the LDS serves together ({0-7, 16-23}, ...) rows r..r+7 at pieces q and q+1
+// (q even); keys 0, 2, 4, 6 over the four rows of one parity keep them in 16 banks groups.
+__device__ __forceinline__ int rt_key(int r) { return ((r >> 1) & 3) << 1; }
 }  // namespace
 
-__global__ __launch_bounds__(256) void router_bf16_kernel(
+__global__ __launch_bounds__(512, 1) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ logits,
     int T, int d, int E, int chunks_per_split) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][RT_BM * RT_ROWB];  // [A|B][row*256]
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int m0 = blockIdx.x * RT_BM, n0 = blockIdx.y * RT_BN;
-  const int wm = wid >> 1, wn = wid & 1;
-  // split-K: this workgroup sums K chunks [c0, c0 + nchunk) into partial plane blockIdx.z
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[RT_SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[RT_SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa2[RT_SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[RT_SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb1[RT_SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb2[RT_SB];
+  auto stage_a = [&](auto S) -> uint8_t* {
+    constexpr int i = decltype(S)::value % 3;
+    if constexpr (i == 0) return sa0;
+    else if constexpr (i == 1) return sa1;
+    else return sa2;
+  };
+  auto stage_b = [&](auto S) -> uint8_t* {
+    constexpr int i = decltype(S)::value % 3;
+    if constexpr (i == 0) return sb0;
+    else if constexpr (i == 1) return sb1;
+    else return sb2;
+  };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 2, wn = wid & 3;
+  const int t0 = blockIdx.x * RT_BM, e0 = blockIdx.y * RT_BN;
   const int c0 = blockIdx.z * chunks_per_split;
-  const int nchunk = min(chunks_per_split, d / RT_BK - c0);
+  const int nc = min(chunks_per_split, d / RT_BK - c0);   // >= 1 by the launcher
   logits += (size_t)blockIdx.z * T * E;
 
-  const uint8_t* a_ptr[RT_LOADS];
-  const uint8_t* b_ptr[RT_LOADS];
-  int lds_off[RT_LOADS];
+  // DMA instruction q of a wave fills 8 rows (1 KB) of group wid + 8 q: lane L lands at
+  // row L/8, slot L%8 and fetches piece (L%8) ^ rt_key(row).  Rows past T or E repeat
+  // the last one; their results are not stored.
+  const uint8_t* xa = reinterpret_cast<const uint8_t*>(x + (size_t)t0 * d + (size_t)c0 * RT_BK);
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(w + (size_t)e0 * d + (size_t)c0 * RT_BK);
+  uint32_t a_off[RT_ADMA], b_off[RT_BDMA];
 #pragma unroll
-  for (int i = 0; i < RT_LOADS; ++i) {
-    int c = tid + i * 256;
-    int row = c / RT_CPR, piece = c % RT_CPR;
-    int ar = min(m0 + row, T - 1), br = min(n0 + row, E - 1);
-    a_ptr[i] = reinterpret_cast<const uint8_t*>(x + (size_t)ar * d + (size_t)c0 * RT_BK) + piece * 16;
-    b_ptr[i] = reinterpret_cast<const uint8_t*>(w + (size_t)br * d + (size_t)c0 * RT_BK) + piece * 16;
-    lds_off[i] = row * RT_ROWB + ((piece ^ (row & 15)) * 16);
+  for (int q = 0; q < RT_ADMA; ++q) {
+    const int row = (wid + 8 * q) * 8 + (lane >> 3), slot = lane & 7;
+    a_off[q] = (uint32_t)(min(t0 + row, T - 1) - t0) * (uint32_t)(d * 2) +
+               ((slot ^ rt_key(row)) << 4);
   }
-  v4i ra[2][RT_LOADS], rb[2][RT_LOADS];
-  auto issue = [&](int slot, int ch) {
 #pragma unroll
-    for (int i = 0; i < RT_LOADS; ++i) {
-      ra[slot][i] = *reinterpret_cast<const v4i*>(a_ptr[i] + (size_t)ch * RT_ROWB);
-      rb[slot][i] = *reinterpret_cast<const v4i*>(b_ptr[i] + (size_t)ch * RT_ROWB);
-    }
+  for (int q = 0; q < RT_BDMA; ++q) {
+    const int row = (wid + 8 * q) * 8 + (lane >> 3), slot = lane & 7;
+    b_off[q] = (uint32_t)(min(e0 + row, E - 1) - e0) * (uint32_t)(d * 2) +
+               ((slot ^ rt_key(row)) << 4);
+  }
+  // chunk c (clamped to the last one, so every call issues the same DMA count)
+  auto dma = [&](auto S, int c) {
+    const size_t cb = (size_t)min(c, nc - 1) * (RT_BK * 2);
+    uint8_t* la = stage_a(S);
+    uint8_t* lb = stage_b(S);
+#pragma unroll
+    for (int q = 0; q < RT_ADMA; ++q) dma16b(xa + cb, a_off[q], la + (wid + 8 * q) * 1024);
+#pragma unroll
+    for (int q = 0; q < RT_BDMA; ++q) dma16b(wb + cb, b_off[q], lb + (wid + 8 * q) * 1024);
   };
-  v4f acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  if (nchunk > 1) issue(1, 1);
-  for (int ch = 0; ch < nchunk; ++ch) {
-    const int slot = ch & 1;
+  v4f acc[4][4];
 #pragma unroll
-    for (int i = 0; i < RT_LOADS; ++i) {
-      *reinterpret_cast<v4i*>(&lds[0][lds_off[i]]) = ra[slot][i];
-      *reinterpret_cast<v4i*>(&lds[1][lds_off[i]]) = rb[slot][i];
-    }
-    __syncthreads();
-    if (ch + 2 < nchunk) issue(slot, ch + 2);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int ks = 0; ks < RT_BK / 32; ++ks) {
-      v8bf af[2], bf[2];
-      const int piece = ks * 4 + (lane >> 4);              // 8 bf16 = one 16-byte piece
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // chunk c in stage c % 3: wait for this wave's DMA of it (one chunk's DMAs came after),
+  // barrier (everyone's DMA of c landed, everyone done with c - 1), refill the stage of
+  // c - 1 with c + 2, then 2 K steps of 32
+  auto body = [&](auto U, int c) {
+    wait_vmcnt<RT_ADMA + RT_BDMA>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    dma(std::integral_constant<int, decltype(U)::value + 2>{}, c + 2);
+    const uint8_t* la = stage_a(U);
+    const uint8_t* lb = stage_b(U);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int ar = wm * 32 + i * 16 + (lane & 15);
-        int br = wn * 32 + i * 16 + (lane & 15);
-        af[i] = *reinterpret_cast<const v8bf*>(&lds[0][ar * RT_ROWB + ((piece ^ (ar & 15)) * 16)]);
-        bf[i] = *reinterpret_cast<const v8bf*>(&lds[1][br * RT_ROWB + ((piece ^ (br & 15)) * 16)]);
+    for (int ks = 0; ks < 2; ++ks) {
+      const int piece = ks * 4 + (lane >> 4);     // 8 bf16
+      v8bf af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wm * 64 + i * 16 + (lane & 15);
+        const int rb = wn * 64 + i * 16 + (lane & 15);
+        af[i] = *reinterpret_cast<const v8bf*>(la + ra * 128 + ((piece ^ rt_key(ra)) << 4));
+        bf[i] = *reinterpret_cast<const v8bf*>(lb + rb * 128 + ((piece ^ rt_key(rb)) << 4));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
-  }
+  };
+  dma(std::integral_constant<int, 0>{}, 0);
+  dma(std::integral_constant<int, 1>{}, 1);
+  int c = 0;
+  for (; c + 3 <= nc; c += 3)
+    static_for<3>([&](auto U) { body(U, c + decltype(U)::value); });
+  static_for<2>([&](auto U) {
+    if (c + decltype(U)::value < nc) body(U, c + decltype(U)::value);
+  });
+  wait_vmcnt<0>();   // the clamped repeat DMAs land before the workgroup's LDS is freed
+
   // C layout of a 16x16 MFMA tile: lane holds column lane%16, rows 4*(lane/16)+r.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      int col = n0 + wn * 32 + j * 16 + (lane & 15);
+    for (int j = 0; j < 4; ++j) {
+      const int col = e0 + wn * 64 + j * 16 + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        int row = m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+        const int row = t0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
         if (row < T && col < E) logits[(size_t)row * E + col] = acc[i][j][r];
       }
     }
@@ -135,24 +177,46 @@ __global__ __launch_bounds__(256) void topk_kernel(float* __restrict__ logits,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   float* row = logits + (size_t)t * E;
-  float key[KPL];
+  float key[KPL], l[KPL];
   bool live[KPL];
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
-    int e = lane + 64 * i;
-    live[i] = e < E;
-    float l = 0.f;
-    if (live[i]) {
-      if (n_part > 1) {
-        const float* pp = part + (size_t)t * E + e;
-        l = pp[0];
-        for (int s = 1; s < n_part; ++s) l += pp[(size_t)s * T * E];
-        row[e] = l;
-      } else {
-        l = row[e];
-      }
+    live[i] = lane + 64 * i < E;
+    l[i] = 0.f;
+  }
+  if (n_part > 1) {
+    // sum the planes in plane order, eight planes' loads in flight at a time
+    const float* pp = part + (size_t)t * E + lane;
+    const size_t ps = (size_t)T * E;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (live[i]) l[i] = pp[64 * i];
+    for (int s0 = 1; s0 < n_part; s0 += 8) {
+      float v[8][KPL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < KPL; ++i)
+          v[u][i] = (s0 + u < n_part && live[i]) ? pp[(size_t)(s0 + u) * ps + 64 * i] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < n_part) {
+#pragma unroll
+          for (int i = 0; i < KPL; ++i) l[i] += v[u][i];
+        }
     }
-    key[i] = live[i] ? l + (bias ? bias[e] : 0.0f) : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (live[i]) row[lane + 64 * i] = l[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (live[i]) l[i] = row[lane + 64 * i];
+  }
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = live[i] ? l[i] + (bias ? bias[e] : 0.0f) : -INFINITY;
   }
   // softmax denominator over every expert
   float m = -INFINITY;
@@ -208,9 +272,11 @@ __global__ void hash_route_kernel(const int64_t* __restrict__ ids, int T, int E,
 // ------------------------------------------------------------------ launchers
 int router_splits(int T, int d, int E, bool bf16) {
   if (!bf16) return 1;
+  // about one workgroup per CU, each with at least RT_MIN_CHUNKS chunks
   const long tiles = (long)((T + RT_BM - 1) / RT_BM) * ((E + RT_BN - 1) / RT_BN);
   const int chunks = d / RT_BK;
-  int want = (int)std::min<long>(std::max<long>(1, (1024 + tiles - 1) / tiles), chunks);
+  const int most = std::max(1, chunks / RT_MIN_CHUNKS);
+  const int want = (int)std::min<long>(std::max<long>(1, 256 / tiles), most);
   const int cps = (chunks + want - 1) / want;
   return (chunks + cps - 1) / cps;
 }
@@ -218,10 +284,12 @@ int router_splits(int T, int d, int E, bool bf16) {
 hipError_t launch_router(const void* x, bool bf16, const void* w, float* logits, int T, int d,
                          int E, float* part, int n_part, hipStream_t s) {
   if (bf16) {
+    // n_part planes of ceil(chunks / n_part) chunks; every plane gets at least one
     const int chunks = d / RT_BK;
     const int cps = (chunks + n_part - 1) / n_part;
+    if (n_part < 1 || (long)(n_part - 1) * cps >= chunks) return hipErrorInvalidValue;
     dim3 grid((T + RT_BM - 1) / RT_BM, (E + RT_BN - 1) / RT_BN, n_part);
-    hipLaunchKernelGGL(router_bf16_kernel, grid, dim3(256), 0, s,
+    hipLaunchKernelGGL(router_bf16_kernel, grid, dim3(512), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
                        n_part > 1 ? part : logits, T, d, E, cps);
   } else {
