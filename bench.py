@@ -157,11 +157,30 @@ def cpu_baseline(w: synth.Workload, inp: dict, n_experts: int = 8):
 
 # ---------------------------------------------------------------------- main
 
+SETTLE_S = 1.5
+
+
+def settle(fn, seconds):
+    """Run fn() untimed for `seconds`: an idle GPU starts at a low engine clock and
+    ramps up under load; timing from a cold start understates steady-state speed."""
+    t_end = time.time() + seconds
+    n = 0
+    while time.time() < t_end:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed steps before the warm-up steps, so the engine "
+                         "clock has left its idle state (it ramps up over tens of ms)")
     ap.add_argument("--workload", default="prefill_fp8",
                     choices=sorted(synth.WORKLOADS) + ["grouped_gemm_fp8", "dense_gemm_fp8",
                                                        "masked_gemm_fp8"])
@@ -187,13 +206,13 @@ def main(argv=None):
 
     import fp8_grouped_gemm_amd as M
     if a.workload == "grouped_gemm_fp8":
-        print(json.dumps(bench_grouped_gemm(M, a.steps, a.warmup)), flush=True)
+        print(json.dumps(bench_grouped_gemm(M, a.steps, a.warmup, a.settle)), flush=True)
         return 0
     if a.workload == "dense_gemm_fp8":
-        print(json.dumps(bench_dense_gemm(M, a.steps, a.warmup)), flush=True)
+        print(json.dumps(bench_dense_gemm(M, a.steps, a.warmup, a.settle)), flush=True)
         return 0
     if a.workload == "masked_gemm_fp8":
-        print(json.dumps(bench_masked_gemm(M, a.steps, a.warmup)), flush=True)
+        print(json.dumps(bench_masked_gemm(M, a.steps, a.warmup, a.settle)), flush=True)
         return 0
     w = synth.WORKLOADS[a.workload]
     if w.m_align != 16:
@@ -214,6 +233,7 @@ def main(argv=None):
     def step():
         M.moe_layer_fwd(desc, weights, x, ids, workspace=ws, y=y, counts=counts)
 
+    settle(step, a.settle)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -263,7 +283,7 @@ def main(argv=None):
         "metric": "MoE layer FP8 grouped-GEMM TFLOPS + tokens/s on 1 MI355X (% roofline)",
         "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "settle_s": a.settle,
         "ms_per_step": round(ms, 4),
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "layer_hbm_frac": round(bytes_ / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -334,7 +354,7 @@ def pmc_summary(dirname):
             for k, d in acc.items()}
 
 
-def bench_grouped_gemm(M, steps, warmup):
+def bench_grouped_gemm(M, steps, warmup, settle_s=SETTLE_S):
     """The standalone FP8 grouped GEMM: 16 groups with Zipf(1.1) sizes summing to 8192
     rows, each padded to 128; N=4096, K=7168; bf16 out.  A 512 MB write between timed
     launches (outside the events) evicts the weights from the last-level cache."""
@@ -353,6 +373,7 @@ def bench_grouped_gemm(M, steps, warmup):
     qb = M.moe_pack_weight_fp8(qb)
     off = torch.from_numpy(offsets).to(dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    settle(lambda: M.grouped_gemm_fp8(qa, sa, qb, sb, off, R, N), settle_s)
     for _ in range(warmup):
         M.grouped_gemm_fp8(qa, sa, qb, sb, off, R, N)
     torch.cuda.synchronize()
@@ -370,6 +391,7 @@ def bench_grouped_gemm(M, steps, warmup):
     tflops = flops / (ms * 1e-3) / 1e12
     return {"metric": "FP8 grouped-GEMM TFLOPS on 1 MI355X (% roofline)", "value": round(tflops, 1),
             "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "settle_s": settle_s,
             "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
             "config": {"workload": "grouped_gemm_fp8: 16 Zipf(1.1) groups sum 8192 (padded to "
@@ -379,10 +401,11 @@ def bench_grouped_gemm(M, steps, warmup):
                          "traffic": None}}
 
 
-def _time_flushed(fn, steps, warmup):
+def _time_flushed(fn, steps, warmup, settle_s=SETTLE_S):
     """Average HIP-event time of fn() with a 512 MB write before each launch (outside the
     events), so that the weights do not stay in the last-level cache."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    settle(fn, settle_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -398,7 +421,7 @@ def _time_flushed(fn, steps, warmup):
     return tot / steps
 
 
-def bench_dense_gemm(M, steps, warmup):
+def bench_dense_gemm(M, steps, warmup, settle_s=SETTLE_S):
     """Dense block-scaled FP8 GEMM at the standalone grouped GEMM's size: M=8192, N=4096,
     K=7168, bf16 out."""
     dev = torch.device("cuda:0")
@@ -408,10 +431,11 @@ def bench_dense_gemm(M, steps, warmup):
     qa, sa = M.moe_quant_fp8(a)
     qb, sb = M.moe_quant_weight_fp8(b)
     qb = M.moe_pack_weight_fp8(qb)
-    ms = _time_flushed(lambda: M.gemm_fp8(qa, sa, qb[0], sb[0]), steps, warmup)
+    ms = _time_flushed(lambda: M.gemm_fp8(qa, sa, qb[0], sb[0]), steps, warmup, settle_s)
     tflops = 2.0 * Mr * N * K / (ms * 1e-3) / 1e12
     return {"metric": "FP8 dense GEMM TFLOPS on 1 MI355X (% roofline)", "value": round(tflops, 1),
             "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "settle_s": settle_s,
             "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
             "config": {"workload": "dense_gemm_fp8: M=8192, N=4096, K=7168, bf16 out"},
@@ -420,7 +444,7 @@ def bench_dense_gemm(M, steps, warmup):
                          "traffic": None}}
 
 
-def bench_masked_gemm(M, steps, warmup):
+def bench_masked_gemm(M, steps, warmup, settle_s=SETTLE_S):
     """GEMM1 of the decode layer over the fixed-capacity layout: the 128-token decode
     routing of 256 experts, capacity ceil(T k / E) * 2 rows per expert, SwiGLU + e4m3
     requant, N = I = 2048, K = d = 7168.  Bound by the touched experts' weight stream."""
@@ -444,14 +468,15 @@ def bench_masked_gemm(M, steps, warmup):
     cnt = torch.clamp(counts, max=cap)
     ms = _time_flushed(lambda: M.grouped_gemm_fp8_masked(qa, sa, weights["w13"], weights["s13"],
                                                           cnt, cap, w.I, swiglu=True),
-                       steps, warmup)
+                       steps, warmup, settle_s)
     touched = int((cnt > 0).sum().item())
     wbytes = touched * (2 * w.I * w.d + 2 * w.I // 128 * w.d // 128 * 4)
     gbs = wbytes / (ms * 1e-3) / 1e9
     tflops = 2.0 * float(cnt.sum().item()) * 2 * w.I * w.d / (ms * 1e-3) / 1e12
     return {"metric": "FP8 masked grouped-GEMM weight stream on 1 MI355X (% roofline)",
             "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
-            "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "warmup": warmup, "settle_s": settle_s, "ms_per_step": round(ms, 4),
+            "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
             "tflops": round(tflops, 2),
             "config": {"workload": f"masked_gemm_fp8: decode GEMM1, E=256 x cap {cap}, "
