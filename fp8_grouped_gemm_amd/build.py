@@ -32,7 +32,7 @@ CFLAGS = [
 # per-source additions
 FILE_FLAGS = {
     # FP8 GEMM: MFMA results in VGPRs, so the per-block promotion FMAs read them without
-    # accvgpr moves (the W4A16 GEMM keeps its accumulators in AGPRs, the default)
+    # accvgpr moves
     "gemm_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

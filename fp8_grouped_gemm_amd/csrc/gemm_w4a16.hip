@@ -7,15 +7,17 @@
 // consumes them, to bf16(fl32(q * s7)) by a byte-permute table lookup (below): the
 // table holds the eight magnitudes' bf16(fl32(m * s7)), each computed with one fp32
 // rounding and the hardware round-to-nearest-even bf16 conversion, so the lookup gives
-// exactly the dequantised weight.  The 32x32x16 bf16 MFMA accumulates in fp32 (AGPRs);
+// exactly the dequantised weight.  The 32x32x16 bf16 MFMA accumulates in fp32;
 // the expansion runs on the vector ALU beside it, software-pipelined one step ahead.
 //
 // Tile: 128 rows x 256 weight rows (plain: 256 output columns, the last column tile
-// possibly half used; SwiGLU: 128 gate + 128 up rows for 128 output columns).  Four
-// waves side by side over the weight rows, each with all 128 rows (64 weight rows per
-// wave).  Gathered activation rows, packed codes
-// and scales arrive by direct global->LDS DMA in three stages, in the same persistent,
-// XCD-aware tile order as the FP8 kernel.
+// possibly half used; SwiGLU: 128 gate + 128 up rows for 128 output columns).  Eight
+// waves (two per SIMD, so one wave's expansion runs beside the other's MFMAs) side by
+// side over the weight rows, each with all 128 rows and 32 weight rows: plain, 32
+// consecutive rows; SwiGLU, 16 gate rows and the 16 up rows of the same output columns,
+// so that one MFMA tile holds both and a lane swap pairs them in the epilogue.
+// Gathered activation rows, packed codes and scales arrive by direct global->LDS DMA in
+// three stages, in the same persistent, XCD-aware tile order as the FP8 kernel.
 #include <type_traits>
 
 #include "common.hpp"
@@ -87,15 +89,16 @@ __device__ __forceinline__ v8bf expand8(uint32_t w, const Tab& t) {
 }  // namespace
 
 template <bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
+__global__ __launch_bounds__(512, 1) void gemm_w4a16_kernel(W4Args args) {
   constexpr int BM = 128, BNB = 256;                // tile rows, weight rows per tile
   constexpr int BNO = SWIGLU ? 128 : 256;           // output columns per tile
   constexpr int NS = 3;                             // DMA stages
   constexpr int ROWB = 256;                         // A bytes per row per K block
-  constexpr int TN = 2;                             // per wave: 2 x 32 weight rows
-  constexpr int A_IN = BM * ROWB / 1024 / 4;        // A DMA instructions per wave: 8
-  constexpr int B_IN = BNB * 64 / 1024 / 4;         // code DMA instructions per wave: 4
-  constexpr int PER_MAX = A_IN + B_IN + 1;          // + the scales
+  constexpr int NW = 8, NT = 512;
+  constexpr int WR = BNB / NW;                      // weight rows per wave: 32
+  constexpr int A_IN = BM * ROWB / 1024 / NW;       // A DMA instructions per wave: 4
+  constexpr int B_IN = WR * 64 / 1024;              // code DMA instructions per wave: 2
+  constexpr int PER_MAX = A_IN + B_IN + 1;          // + the scales (even waves)
   constexpr int A_BYTES = BM * ROWB;                // 32 KB
   constexpr int BR_OFF = A_BYTES;                   // codes: 256 rows x 64 B
   constexpr int SC_OFF = BR_OFF + BNB * 64;         // scales: 256 floats
@@ -118,26 +121,26 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
   const int G = args.G, K = args.K, N = args.N, KB = K / 128;
   const int NBtot = SWIGLU ? 2 * N : N;
   const int tiles_n = (N + BNO - 1) / BNO;
-  build_tile_map<BM>(tm, args.offsets, G);
+  build_tile_map<BM, BM, NT>(tm, args.offsets, G);
   const int total = tm.start[G] * tiles_n;
   const int P = gridDim.x, b = blockIdx.x;
   const int v = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
   const uint32_t lds0 = lds_addr(&lds[0][0]);
 
-  // weight row of tile row r = 64 * wave + s: plain n0 + r (past N: repeats row N-1,
-  // unused); SwiGLU gate rows n0 + 32 * wave + s (s < 32) and up rows
-  // N + n0 + 32 * wave + s - 32 (s >= 32)
+  // weight row of tile row r = 32 * wave + s: plain n0 + r (past N: repeats row N-1,
+  // unused); SwiGLU gate rows n0 + 16 * wave + s (s < 16) and the up rows of the same
+  // columns, N + n0 + 16 * wave + s - 16 (s >= 16)
   auto wrow = [&](int r, int n0) {
     if (!SWIGLU) return min(n0 + r, N - 1);
-    const int w = r >> 6, s = r & 63;
-    return s < 32 ? n0 + 32 * w + s : N + n0 + 32 * w + s - 32;
+    const int w = r >> 5, s = r & 31;
+    return s < 16 ? n0 + 16 * w + s : N + n0 + 16 * w + s - 16;
   };
 
   // one tile whose real rows lie in its first TM 32-row blocks
   auto run_tile = [&](auto TMC, int g, int row0, int n_valid, int n0) {
     constexpr int TM = decltype(TMC)::value;
     const int ncols = min(BNO, N - n0);            // plain N % 256 == 128: last tile half
-    const bool wactive = SWIGLU || wid * 64 < ncols;  // else: repeated rows, not stored
+    const bool wactive = SWIGLU || wid * WR < ncols;  // else: repeated rows, not stored
 
     // A: an instruction fills 4 rows of 256 B; lane L lands at row L/16, slot L%16 and
     // fetches 16-byte piece (L%16) ^ akey(row), the XOR swizzle read back below.
@@ -149,20 +152,23 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
                  (((lane & 15) ^ akey(row)) << 4);
     }
     const int a_cnt = min(max((n_valid - wid * A_IN * 4 + 3) / 4, 0), A_IN);
-    const int per = a_cnt + B_IN + 1;
     // codes: an instruction fills 16 weight rows of 64 B (row L/4, slot L%4, holding
-    // piece (L%4) ^ ckey(row)); every wave fetches its own 64 rows and their 64 scales
+    // piece (L%4) ^ ckey(row)); every wave fetches its own 32 rows, and each even wave
+    // the 64 scales of its rows and the next wave's (one row per lane)
+    const bool scales = (wid & 1) == 0;
+    const int per = a_cnt + B_IN + (scales ? 1 : 0);
     const uint8_t* b_src[B_IN];
 #pragma unroll
     for (int i = 0; i < B_IN; ++i) {
-      const int r = wid * 64 + i * 16 + (lane >> 2);
+      const int r = wid * WR + i * 16 + (lane >> 2);
       b_src[i] = args.B + ((size_t)g * NBtot + wrow(r, n0)) * (K / 2) +
                  (((lane & 3) ^ ckey(r)) << 4);
     }
-    const float* s_src = args.s7 + ((size_t)g * NBtot + wrow(wid * 64 + lane, n0)) * KB;
+    const float* s_src =
+        args.s7 + ((size_t)g * NBtot + wrow(min(wid * WR + lane, BNB - 1), n0)) * KB;
     const uint32_t m_a = lds0 + (uint32_t)wid * (A_IN * 1024);
     const uint32_t m_b = lds0 + BR_OFF + (uint32_t)wid * (B_IN * 1024);
-    const uint32_t m_s = lds0 + SC_OFF + (uint32_t)wid * 256;
+    const uint32_t m_s = lds0 + SC_OFF + (uint32_t)wid * (WR * 4);
     auto issue = [&](int st, int kb) {
       const uint32_t so = (uint32_t)st * STAGE;
 #pragma unroll
@@ -170,16 +176,14 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
         if (i < a_cnt) dma16(a_src[i] + (size_t)kb * ROWB, m_a + so + i * 1024);
 #pragma unroll
       for (int i = 0; i < B_IN; ++i) dma16(b_src[i] + (size_t)kb * 64, m_b + so + i * 1024);
-      dma4(s_src + kb, m_s + so);
+      if (scales) dma4(s_src + kb, m_s + so);
     };
 
-    v16f acc[TM][TN];
+    v16f acc[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
     // K loop: buffers hold blocks kb, kb+1, kb+2; one barrier per block publishes block
     // kb and certifies that every wave is done with block kb-1, whose buffer is refilled.
@@ -193,20 +197,16 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
       const uint8_t* L = lds[st];
       // MFMA step kk takes k = 64 hf + 8 kk + e from lane (l32, hf): code word 8 hf + kk
       // of the weight row and 16-byte piece 8 hf + kk of the A row, one k order for both.
-      v4i raw[TN][2];
-      Tab tab[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wid * 64 + j * 32 + l32;
+      v4i raw[2];
+      Tab tab;
+      {
+        const int r = wid * WR + l32;
         const uint8_t* src = L + BR_OFF + r * 64;
-        raw[j][0] = *reinterpret_cast<const v4i*>(src + (((2 * hf) ^ ckey(r)) << 4));
-        raw[j][1] = *reinterpret_cast<const v4i*>(src + (((2 * hf + 1) ^ ckey(r)) << 4));
-        tab[j] = make_tab(reinterpret_cast<const float*>(L + SC_OFF)[r]);
+        raw[0] = *reinterpret_cast<const v4i*>(src + (((2 * hf) ^ ckey(r)) << 4));
+        raw[1] = *reinterpret_cast<const v4i*>(src + (((2 * hf + 1) ^ ckey(r)) << 4));
+        tab = make_tab(reinterpret_cast<const float*>(L + SC_OFF)[r]);
       }
-      auto expand_step = [&](int kk, v8bf* bf) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = expand8((uint32_t)raw[j][kk >> 2][kk & 3], tab[j]);
-      };
+      auto expand_step = [&](int kk) { return expand8((uint32_t)raw[kk >> 2][kk & 3], tab); };
       auto read_step = [&](int kk, v8bf* af) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -215,32 +215,29 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
                                                  (((8 * hf + kk) ^ akey(row)) << 4));
         }
       };
-      // software pipeline over the 8 steps: while the TM x TN MFMAs of step kk run, the
-      // wave reads the A fragments and expands the weights of step kk + 1
-      v8bf af[2][TM], bf[2][TN];
+      // software pipeline over the 8 steps: while the TM MFMAs of step kk run, the wave
+      // reads the A fragments and expands the weights of step kk + 1
+      v8bf af[2][TM], bf[2];
       read_step(0, af[0]);
-      expand_step(0, bf[0]);
+      bf[0] = expand_step(0);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int c = kk & 1;
         if (kk + 1 < 8) {
           read_step(kk + 1, af[c ^ 1]);
-          expand_step(kk + 1, bf[c ^ 1]);
+          bf[c ^ 1] = expand_step(kk + 1);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j],
-                                                                0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c], acc[i], 0, 0, 0);
         // issue order: each MFMA followed by a share of the next step's LDS reads and
         // expansion (left alone, the scheduler sinks them to their uses)
         if (kk + 1 < 8) {
 #pragma unroll
-          for (int m = 0; m < TM * TN; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-            if (m < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // DS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 28 / (TM * TN) + 1, 0);  // VALU
+          for (int m = 0; m < TM; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 15 / TM + 1, 0);    // VALU
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -252,7 +249,9 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
     __syncthreads();
     uint8_t* ot = &lds[0][0];
     constexpr int OB = BNO * 2;
-    // accumulator element r of lane (l32, hf): row 8 (r / 4) + 4 hf + r % 4, column l32
+    // accumulator element r of lane (l32, hf): row 8 (r / 4) + 4 hf + r % 4, column l32.
+    // SwiGLU: columns 0-15 are gate rows, 16-31 the up rows of the same outputs; lane
+    // l32 < 16 takes the up value from lane l32 + 16.
     if (wactive) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -260,22 +259,22 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a16_kernel(W4Args args) {
         for (int r = 0; r < 16; ++r) {
           const int trow = i * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
           if (SWIGLU) {
-            const int tcol = wid * 32 + l32;
-            const float hv = silu(acc[i][0][r]) * acc[i][1][r];
-            *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(hv);
-          } else {
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const int tcol = wid * 64 + j * 32 + l32;
-              *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(acc[i][j][r]);
+            const float up = __shfl_xor(acc[i][r], 16, 64);
+            if (l32 < 16) {
+              const int tcol = wid * 16 + l32;
+              const float hv = silu(acc[i][r]) * up;
+              *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(hv);
             }
+          } else {
+            const int tcol = wid * WR + l32;
+            *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(acc[i][r]);
           }
         }
     }
     __syncthreads();
     const int CPR = ncols / 8;                     // 16-byte chunks per output row
     uint8_t* C = reinterpret_cast<uint8_t*>(args.C);
-    for (int c = tid; c < n_valid * CPR; c += 256) {
+    for (int c = tid; c < n_valid * CPR; c += NT) {
       const int trow = c / CPR, ch = c % CPR;
       *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) =
           *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
@@ -319,9 +318,9 @@ hipError_t launch_gemm_w4a16(const uint16_t* A, const int32_t* a_rows, int a_row
   if (grid >= 8) grid = grid / 8 * 8;
   if (grid < 1) grid = 1;
   if (swiglu)
-    hipLaunchKernelGGL(gemm_w4a16_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gemm_w4a16_kernel<true>, dim3((unsigned)grid), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL(gemm_w4a16_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gemm_w4a16_kernel<false>, dim3((unsigned)grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
