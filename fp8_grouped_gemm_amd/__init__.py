@@ -72,15 +72,16 @@ def moe_rows_bound(T: int, k: int, E: int, m_align: int) -> int:
 # -------------------------------------------------------------------- routing
 
 def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor, k: int,
-              renorm: bool = False):
-    """Router logits + biased softmax top-k.  Returns (topk_idx, topk_w, logits)."""
+              renorm: bool = False, use_workspace: bool = True):
+    """Router logits + biased softmax top-k.  Returns (topk_idx, topk_w, logits).
+    use_workspace=False passes no workspace (the logits GEMM then runs without split-K)."""
     T, d = x.shape
     E = w_router.shape[0]
     dev = x.device
     logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    nws = _lib_().moe_route_workspace_size(T, d, E, _dt(x))
+    nws = _lib_().moe_route_workspace_size(T, d, E, _dt(x)) if use_workspace else 0
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     _lib.check(_lib_().moe_route(_ptr(x), _dt(x), _ptr(w_router), _ptr(bias), T, d, E, k,
                                  MOE_ROUTE_RENORM if renorm else 0, _ptr(logits), _ptr(idx),

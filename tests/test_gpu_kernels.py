@@ -136,20 +136,24 @@ def test_route_from_logits(T, E, k, ties, renorm):
     np.testing.assert_allclose(to_np(w), wo, rtol=2e-5, atol=0)
 
 
-@pytest.mark.parametrize("dtype,T,d,E,k", [(torch.bfloat16, 200, 512, 256, 8),
-                                           (torch.bfloat16, 70, 7168, 64, 6),
-                                           (torch.bfloat16, 128, 7168, 256, 8),
-                                           (torch.bfloat16, 300, 7168, 256, 8),
-                                           (torch.float32, 256, 256, 8, 2)])
-def test_router_logits(dtype, T, d, E, k):
+@pytest.mark.parametrize("dtype,T,d,E,k,ws", [(torch.bfloat16, 200, 512, 256, 8, True),
+                                              (torch.bfloat16, 70, 7168, 64, 6, True),
+                                              (torch.bfloat16, 128, 7168, 256, 8, True),
+                                              (torch.bfloat16, 300, 7168, 256, 8, True),
+                                              (torch.bfloat16, 1, 128, 300, 4, True),
+                                              (torch.bfloat16, 129, 1024, 520, 8, True),
+                                              (torch.bfloat16, 257, 2048, 256, 8, False),
+                                              (torch.float32, 256, 256, 8, 2, True)])
+def test_router_logits(dtype, T, d, E, k, ws):
     """Logits within the fp32 accumulation bound; routing equal to the oracle's own
     routing wherever the k-th and (k+1)-th keys are further apart than that bound (and
-    a valid choice where they are not).  Covers the split-K partial logits."""
-    note(f"router logits {dtype} T={T} d={d} E={E} k={k}")
+    a valid choice where they are not).  Covers the split-K partial logits, partial
+    token and expert tiles, and the unsplit GEMM when no workspace is given."""
+    note(f"router logits {dtype} T={T} d={d} E={E} k={k} ws={ws}")
     x = synth.normal((T, d), 9, "x", dtype=dtype)
     w = synth.normal((E, d), 9, "w_gate_router", std=d ** -0.5, dtype=dtype)
     b = synth.uniform((E,), -0.01, 0.01, 9, "bias")
-    idx, gw, logits = M.moe_route(x.to(dev()), w.to(dev()), b.to(dev()), k)
+    idx, gw, logits = M.moe_route(x.to(dev()), w.to(dev()), b.to(dev()), k, use_workspace=ws)
     ref = O.router_logits(x.float().numpy(), w.float().numpy())
     # fp32 accumulation of d exact products: |err| <= d * 2^-24 * sum|x_i w_i|
     bound = d * 2.0 ** -24 * (np.abs(x.float().numpy()) @ np.abs(w.float().numpy()).T)
