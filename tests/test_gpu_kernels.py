@@ -374,6 +374,44 @@ def test_grouped_gemm_fp8_short_k(K, sizes, m_align, swiglu):
         _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
 
 
+@pytest.mark.parametrize("case", ["max_k", "max_groups"])
+def test_grouped_gemm_fp8_limits(case):
+    """The largest K the kernel accepts (16384: the tile's activation-scale table full)
+    and the largest group count (1024, mixed small and large groups, so both tile lists
+    and their interleave span the whole tile map)."""
+    if case == "max_k":
+        sizes, N, K, m_align = [3, 0, 150, 20], 128, 16384, 16
+    else:
+        rng = np.random.default_rng(12)
+        sizes = rng.integers(0, 24, 1024)
+        sizes[rng.choice(1024, 12, replace=False)] = rng.integers(100, 300, 12)
+        sizes = sizes.tolist()
+        N, K, m_align = 128, 256, 16
+    for swiglu in (False, True):
+        note(f"gemm fp8 limits {case} swiglu={swiglu}")
+        a, b, offsets, R = _gemm_case(sizes, N, K, m_align, 41, swiglu)
+        qa, sa = M.moe_quant_fp8(a.to(dev()))
+        qb, sb = M.moe_quant_weight_fp8(b.to(dev()))
+        qao, sao = OC.quant_fp8_act(a.numpy())
+        qbo, sbo = OC.quant_fp8_weight(b.numpy())
+        off_d = torch.from_numpy(offsets).to(dev())
+        ref = O.grouped_gemm_fp8(qao, sao, qbo, sbo, offsets)
+        live = np.zeros(R, bool)
+        for g in range(len(sizes)):
+            live[offsets[g]:offsets[g] + sizes[g]] = True
+        if not swiglu:
+            c = M.grouped_gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb), sb, off_d, R, N)
+            beyond, raw = error_ratios(to_np(c)[live], ref[live])
+            assert beyond <= TOL, beyond
+        else:
+            codes, sc = M.grouped_gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb), sb, off_d, R, N,
+                                           swiglu=True)
+            A = OC.dequant_fp8_act(qao, sao)
+            Bd = OC.dequant_fp8_weight(qbo, sbo)
+            sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)
+            _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
+
+
 @pytest.mark.parametrize("Mrows,K", [(0, 512), (1, 512), (200, 512), (333, 512),
                                      (333, 128), (40, 256), (333, 640)])
 def test_gemm_fp8_dense(Mrows, K):
