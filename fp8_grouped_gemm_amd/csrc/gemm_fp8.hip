@@ -205,17 +205,37 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       for (int q = 0; q < ADMA; ++q) dma16b(base, a_voff[q], st + a_m[q]);
     };
 
-    // ---- the tile's row scales, transposed into LDS [kb][row]: thread (row, q) fetches
-    // blocks 4q .. 4q+3 of one row
+    // ---- the tile's row scales, transposed into LDS [kb][row]: item p = (row, q) holds
+    // blocks 4q .. 4q+3 of one row.  All of a thread's loads are issued before any of
+    // its LDS writes, so the latency is paid once, not item by item.
     {
-      const int nq = (KB + 3) / 4;
-      for (int p = tid; p < BM * nq; p += NT) {
-        const int row = p % BM, q = p / BM;
-        const float* src = args.sA + (size_t)row_src[row] * KB;
+      constexpr int TAB_IT = 4;                    // items per thread per round
+      const int tab_items = BM * ((KB + 3) / 4);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(args.sA), (short)0, -1, 0x00020000);
+      for (int p0 = 0; p0 < tab_items; p0 += TAB_IT * NT) {
+        float tv[TAB_IT][4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int kb = min(4 * q + t, KB - 1);
-          tab[kb * BMB + row] = src[kb];
+        for (int it = 0; it < TAB_IT; ++it) {
+          const int p = p0 + tid + it * NT;
+          if (p < tab_items) {
+            const int row = p % BM, q = p / BM;
+            const uint32_t base = (uint32_t)row_src[row] * (uint32_t)KB;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              tv[it][t] = __builtin_bit_cast(
+                  float, __builtin_amdgcn_raw_buffer_load_b32(
+                             rs, (base + (uint32_t)min(4 * q + t, KB - 1)) * 4u, 0, 0));
+          }
+        }
+#pragma unroll
+        for (int it = 0; it < TAB_IT; ++it) {
+          const int p = p0 + tid + it * NT;
+          if (p < tab_items) {
+            const int row = p % BM, q = p / BM;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) tab[min(4 * q + t, KB - 1) * BMB + row] = tv[it][t];
+          }
         }
       }
     }
