@@ -205,36 +205,51 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       for (int q = 0; q < ADMA; ++q) dma16b(base, a_voff[q], st + a_m[q]);
     };
 
-    // ---- the tile's row scales, transposed into LDS [kb][row]: item p = (row, q) holds
-    // blocks 4q .. 4q+3 of one row.  All of a thread's loads are issued before any of
-    // its LDS writes, so the latency is paid once, not item by item.
+    // ---- the tile's row scales, transposed into LDS [kb][row].  Item (row, q) holds
+    // blocks 4q .. 4q+3 of one row, fetched as one 16-byte load; consecutive lanes take
+    // 16 consecutive rows, then the next q, so one wave instruction covers 16 rows x 64
+    // contiguous bytes instead of 64 scattered rows.  A thread issues all loads of a
+    // round before its LDS writes, so the latency is paid once per round.
     {
       constexpr int TAB_IT = 4;                    // items per thread per round
-      const int tab_items = BM * ((KB + 3) / 4);
+      const int nq = (KB + 3) / 4;
+      const int tab_items = BM * nq;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(args.sA), (short)0, -1, 0x00020000);
+      auto item = [&](int p, int& row, int& q) {
+        const int rest = p >> 4;
+        q = rest % nq;
+        row = (rest / nq) * 16 + (p & 15);
+      };
       for (int p0 = 0; p0 < tab_items; p0 += TAB_IT * NT) {
-        float tv[TAB_IT][4];
+        v4i tv[TAB_IT];
 #pragma unroll
         for (int it = 0; it < TAB_IT; ++it) {
           const int p = p0 + tid + it * NT;
           if (p < tab_items) {
-            const int row = p % BM, q = p / BM;
+            int row, q;
+            item(p, row, q);
             const uint32_t base = (uint32_t)row_src[row] * (uint32_t)KB;
+            if (4 * q + 3 < KB) {
+              tv[it] = __builtin_bit_cast(
+                  v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, (base + 4 * q) * 4u, 0, 0));
+            } else {                                 // the row's last, partial chunk
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              tv[it][t] = __builtin_bit_cast(
-                  float, __builtin_amdgcn_raw_buffer_load_b32(
-                             rs, (base + (uint32_t)min(4 * q + t, KB - 1)) * 4u, 0, 0));
+              for (int t = 0; t < 4; ++t)
+                tv[it][t] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+                    rs, (base + (uint32_t)min(4 * q + t, KB - 1)) * 4u, 0, 0);
+            }
           }
         }
 #pragma unroll
         for (int it = 0; it < TAB_IT; ++it) {
           const int p = p0 + tid + it * NT;
           if (p < tab_items) {
-            const int row = p % BM, q = p / BM;
+            int row, q;
+            item(p, row, q);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) tab[min(4 * q + t, KB - 1) * BMB + row] = tv[it][t];
+            for (int t = 0; t < 4; ++t)
+              if (4 * q + t < KB) tab[(4 * q + t) * BMB + row] = __int_as_float(tv[it][t]);
           }
         }
       }
