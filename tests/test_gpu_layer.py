@@ -48,11 +48,13 @@ def _near_ties(logits32, bias, k, margin):
     return (srt[:, k - 1] - srt[:, k]) < margin
 
 
-def run_layer_case(w: synth.Workload, tokens=None):
-    note(f"layer {w.name} T={w.T} d={w.d} E={w.E} k={w.k} I={w.I} mode={w.mode}")
+def run_layer_case(w: synth.Workload, tokens=None, cap_factor=0.0):
+    note(f"layer {w.name} T={w.T} d={w.d} E={w.E} k={w.k} I={w.I} mode={w.mode} "
+         f"cap_factor={cap_factor}")
     inp = synth.layer_inputs(w)
     gw = _gpu_weights(w, inp)
-    desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align)
+    desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align,
+                       capacity_factor=cap_factor)
     x = inp["x"].to(dev())
     ids = inp.get("token_ids")
     y, counts = M.moe_layer_fwd(desc, gw, x, ids.to(dev()) if ids is not None else None)
@@ -63,7 +65,7 @@ def run_layer_case(w: synth.Workload, tokens=None):
                           bias=None if w.route == "hash" else inp["bias"].numpy(),
                           token_ids=None if ids is None else ids.numpy(),
                           experts=_oracle_experts(w, inp), tokens=tokens,
-                          keep=(w.mode == "fp8"))
+                          keep=(w.mode == "fp8"), cap_factor=cap_factor)
     rows = np.arange(w.T) if tokens is None else np.asarray(tokens)
     if w.route == "score":
         amb = _near_ties(ref["logits"].astype(np.float32), inp["bias"].numpy(), w.k, 1e-5)
@@ -78,12 +80,12 @@ def run_layer_case(w: synth.Workload, tokens=None):
         beyond, raw = error_ratios(yg, yr, rounding=0.0)
         print(f"raw={raw:.3e}")
         assert raw <= TOL
-        return
+        return ref
     if w.mode == "fp8":
         e = fp8_layer_errors(yg, ref, keep, w.T, w.k)
         print(f"errors {e} ambiguous_tokens={int(amb.sum())}")
         assert e["beyond_flip"] <= TOL
-        return
+        return ref
     # w4a16: bf16 output of y plus the bf16 expert rows it sums
     r = 0.5 * ulp_bf16(yr)
     wk = np.asarray(ref["w"]).reshape(w.T, w.k)
@@ -95,6 +97,7 @@ def run_layer_case(w: synth.Workload, tokens=None):
     beyond, raw = error_ratios(yg, yr, rounding=r)
     print(f"beyond={beyond:.3e} raw={raw:.3e} ambiguous={int(amb.sum())}")
     assert beyond <= TOL
+    return ref
 
 
 def test_layer_tiny_fp32():
@@ -109,6 +112,20 @@ def test_layer_small_fp8():
 def test_layer_small_fp8_many_experts():
     run_layer_case(synth.Workload("small_fp8_e64", T=200, d=384, E=64, k=6, I=128, mode="fp8",
                                   m_align=32, seed=3))
+
+
+@pytest.mark.parametrize("mode", ["fp8", "fp32"])
+def test_layer_capacity_drop(mode):
+    """Capacity floor(ceil(T*k/E) * 1.0) with skewed routing: the favoured experts
+    overflow and their late slots are dropped (contribute nothing)."""
+    w = synth.Workload(f"cap_{mode}", T=96, d=256, E=8, k=2, I=256, mode=mode,
+                       skew_frac=0.25, skew_add=2.0, m_align=16, seed=5)
+    cap = M.moe_capacity(w.T, w.k, w.E, 1.0)
+    assert cap == -(-w.T * w.k // w.E)
+    ref = run_layer_case(w, cap_factor=1.0)
+    dropped = int(np.maximum(np.asarray(ref["counts"]) - cap, 0).sum())
+    print(f"capacity {cap}, dropped slots {dropped}")
+    assert dropped > 0
 
 
 def test_layer_small_w4a16_hash():
