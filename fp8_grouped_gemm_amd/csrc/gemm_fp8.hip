@@ -127,6 +127,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
   __shared__ __attribute__((aligned(1024))) uint8_t st3[A_STAGE];
   __shared__ __attribute__((aligned(1024))) float tab[TAB_FLOATS > OUT_FLOATS ? TAB_FLOATS : OUT_FLOATS];
   __shared__ int row_src[BMB];
+  // product tables: the tile's two weight-scale rows, table t at [t * PT_KB + kb]
+  constexpr int PT_KB = TAB_FLOATS / (2 * BMB);
+  __shared__ float sbt[2 * PT_KB];
   auto stage = [&](auto S) -> uint8_t* {
     constexpr int sidx = decltype(S)::value % NSA;
     if constexpr (sidx == 0) return st0;
@@ -159,8 +162,13 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
   const int P = gridDim.x, b = blockIdx.x;
   const int v = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
 
-  auto run_tile = [&](auto BMC, int g, int row0, int row_end, int n0) {
+  // PROD (K <= PT_KB blocks): the table holds each row scale already multiplied by the
+  // weight scale of the block, one table per 128-column weight block the tile touches
+  // (plain: the tile's two halves; SwiGLU: gate and up), so promotion is a bare FMA.
+  // The product is rounded once, as the in-loop product of the other form is.
+  auto run_tile = [&](auto BMC, auto PRODC, int g, int row0, int row_end, int n0) {
     constexpr int BM = decltype(BMC)::value;
+    constexpr bool PROD = decltype(PRODC)::value;
     constexpr int TM = BM / 16;                    // 16-row MFMA tiles per wave
     // weight ring: blocks kb .. kb+DB-1.  Small tiles only stream weights, so they keep
     // more blocks in flight (their accumulators are few).
@@ -182,6 +190,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
         src = sr < 0 ? 0 : sr / args.a_row_div;
       }
       row_src[tid] = src;
+    }
+    if constexpr (PROD) {
+      // weight-scale rows of the tables; plain: the second half's block (clamped for a
+      // half last tile, whose second-half waves use the first table)
+      const int cb0 = n0 / 128;
+      const int cb1 = SWIGLU ? (N + n0) / 128 : min(cb0 + 1, RB - 1);
+      if (tid < 2 * PT_KB) {
+        const int t = tid / PT_KB, kb = tid - t * PT_KB;
+        if (kb < KB) sbt[tid] = sB[((size_t)g * RB + (t ? cb1 : cb0)) * KB + kb];
+      }
     }
     __syncthreads();
 
@@ -248,8 +266,18 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
             int row, q;
             item(p, row, q);
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (4 * q + t < KB) tab[(4 * q + t) * BMB + row] = __int_as_float(tv[it][t]);
+            for (int t = 0; t < 4; ++t) {
+              const int kb = 4 * q + t;
+              if (kb < KB) {
+                const float a = __int_as_float(tv[it][t]);
+                if constexpr (PROD) {
+                  tab[kb * BMB + row] = a * sbt[kb];
+                  tab[(PT_KB + kb) * BMB + row] = a * sbt[PT_KB + kb];
+                } else {
+                  tab[kb * BMB + row] = a;
+                }
+              }
+            }
           }
         }
       }
@@ -283,8 +311,10 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
         const v4i hi = *reinterpret_cast<const v4i*>(p + 1024 + b_lane);
         bq[slot][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      sbq[slot][0] = sb0[kb];
-      sbq[slot][1] = SWIGLU ? sb1[kb] : 0.f;
+      if constexpr (!PROD) {
+        sbq[slot][0] = sb0[kb];
+        sbq[slot][1] = SWIGLU ? sb1[kb] : 0.f;
+      }
       asm volatile("" ::: "memory");
     };
 
@@ -300,14 +330,22 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     // fragments, published by the barrier RA steps before the block ends.  Promotion of
     // a step's partials runs one step behind its MFMAs (rings of PR), across blocks.
     // Ring phases are compile-time because the K loop is unrolled by DB blocks.
+    // PROD: a step's promotion reads its scale set straight from the ring (SR sets, one
+    // more than the fragments, so the set is still there one step later); otherwise
+    // the scale products are formed in the step (cq).
     constexpr int RA = TM < 2 ? TM : 2;
     constexpr int AR = 3;                          // divides UNR * TM
+    constexpr int SR = PROD ? RA + 2 : AR;
     constexpr int PR = (TM % 2 == 0) ? 2 : 3;      // divides UNR * TM
-    static_assert((UNR * TM) % AR == 0 && (UNR * TM) % PR == 0, "ring phases");
+    constexpr int NSC = (PROD && SWIGLU) ? 2 : 1;  // scale sets per step
+    static_assert((UNR * TM) % AR == 0 && (UNR * TM) % PR == 0 && (UNR * TM) % SR == 0,
+                  "ring phases");
     v8i af[AR];
-    v4f sa[AR];
+    v4f sa[SR][NSC];
     v4f pp[PR][TN];
-    v4f cq[PR][2];
+    v4f cq[PROD ? 1 : PR][2];
+    // plain PROD: the table of this wave's half
+    const float* tabw = tab + ((PROD && !SWIGLU && wcol >= 128) ? PT_KB * BMB : 0);
     auto rd_a = [&](const uint8_t* L, int i) {
       const int row = i * 16 + (lane & 15);
       const uint8_t* base = L + row * 128;
@@ -315,13 +353,22 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ swz(row)) << 4));
       return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    auto rd_s = [&](int kbx, int i) {
-      return *reinterpret_cast<const v4f*>(tab + kbx * BMB + i * 16 + (lane >> 4) * 4);
+    auto rd_s = [&](int kbx, int i, int t = 0) {
+      return *reinterpret_cast<const v4f*>(tabw + (t * PT_KB + kbx) * BMB + i * 16 +
+                                           (lane >> 4) * 4);
     };
-    auto promote = [&](int slot, int ii) {
+    auto rd_sets = [&](int sslot, int kbx, int i) {
+#pragma unroll
+      for (int t = 0; t < NSC; ++t) sa[sslot][t] = rd_s(kbx, i, t);
+    };
+    // promote the partials in pp[slot] (scales: ring set sslot, PROD) into row tile ii
+    auto promote = [&](int slot, int sslot, int ii) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const v4f c = cq[slot][(SWIGLU && j >= TN / 2) ? 1 : 0];
+        const int h = (SWIGLU && j >= TN / 2) ? 1 : 0;
+        v4f c;
+        if constexpr (PROD) c = sa[sslot][NSC > 1 ? h : 0];
+        else c = cq[slot][h];
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[ii][j][r] = fmaf(c[r], pp[slot][j][r], acc[ii][j][r]);
       }
@@ -340,7 +387,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* L = stage(U);
       const uint8_t* Ln = stage(std::integral_constant<int, u + 1>{});
-      const float sbA = sbq[ub][0], sbB = SWIGLU ? sbq[ub][1] : sbq[ub][0];
+      [[maybe_unused]] const float sbA = sbq[ub][0];
+      [[maybe_unused]] const float sbB = SWIGLU ? sbq[ub][1] : sbq[ub][0];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int gs = g0 + i;
@@ -354,26 +402,28 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
         }
         {
           const int ni = i + RA;
-          const int slot = (gs + RA) % AR;
+          const int slot = (gs + RA) % AR, sslot = (gs + RA) % SR;
           if (ni < TM) {
             af[slot] = rd_a(L, ni);
-            sa[slot] = rd_s(kb, ni);
+            rd_sets(sslot, kb, ni);
           } else {
             af[slot] = rd_a(Ln, ni - TM);
-            sa[slot] = rd_s(min(kb + 1, KB - 1), ni - TM);
+            rd_sets(sslot, min(kb + 1, KB - 1), ni - TM);
           }
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           pp[gs % PR][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               af[gs % AR], bq[ub][j], zero, 0, 0, 0, 0, 0, 0);
-        cq[gs % PR][0] = sa[gs % AR] * sbA;
-        cq[gs % PR][1] = sa[gs % AR] * sbB;
+        if constexpr (!PROD) {
+          cq[gs % PR][0] = sa[gs % SR][0] * sbA;
+          cq[gs % PR][1] = sa[gs % SR][0] * sbB;
+        }
         // the previous step's partials (before the tile's first block: zeros)
-        promote((gs + UNR * TM - 1) % PR, i > 0 ? i - 1 : TM - 1);
+        promote((gs + UNR * TM - 1) % PR, (gs + UNR * TM - 1) % SR, i > 0 ? i - 1 : TM - 1);
         // issue order inside a step: next fragment's reads, then each MFMA followed by
         // four promotion FMAs that run in its shadow; nothing moves across steps
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + NSC, 0);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -398,15 +448,22 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
       af[i] = rd_a(stage(std::integral_constant<int, 0>{}), i);
-      sa[i] = rd_s(0, i);
+      rd_sets(i, 0, i);
     }
+    // the first step promotes zeros: partials and scales of the sets not yet read
 #pragma unroll
-    for (int p = 0; p < PR; ++p) {
+    for (int i = RA; i < SR; ++i)
+#pragma unroll
+      for (int t = 0; t < NSC; ++t) sa[i][t] = zero;
+#pragma unroll
+    for (int p = 0; p < (PROD ? 1 : PR); ++p) {
       cq[p][0] = zero;
       cq[p][1] = zero;
+    }
+#pragma unroll
+    for (int p = 0; p < PR; ++p)
 #pragma unroll
       for (int j = 0; j < TN; ++j) pp[p][j] = zero;
-    }
     int kb = 0;
     for (; kb + UNR <= KB; kb += UNR)
       static_for<UNR>([&](auto U) { body(U, kb + decltype(U)::value); });
@@ -422,16 +479,19 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int e = 0; e < 8; ++e) x ^= bq[d][j][e];
-        x ^= __float_as_int(sbq[d][0]) ^ __float_as_int(sbq[d][1]);
+        if constexpr (!PROD) x ^= __float_as_int(sbq[d][0]) ^ __float_as_int(sbq[d][1]);
       }
       static_cast<int*>(args.C)[tid] = x;
     }
     {
       // the last block's last step
       const int glast = ((KB - 1) % UNR) * TM + TM - 1;
-      if (glast % PR == 0) promote(0, TM - 1);
-      else if (glast % PR == 1) promote(1, TM - 1);
-      else if constexpr (PR > 2) promote(2, TM - 1);
+      static_for<PR>([&](auto P_) {
+        static_for<SR>([&](auto S_) {
+          constexpr int pv = decltype(P_)::value, sv = decltype(S_)::value;
+          if (glast % PR == pv && glast % SR == sv) promote(pv, sv, TM - 1);
+        });
+      });
     }
     wait_vmcnt<0>();  // the last (clamped) activation DMAs land before LDS is reused
     lds_barrier();
@@ -540,10 +600,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     const int r0 = __builtin_amdgcn_readfirstlane(group_row0(tm, gu));
     const int n0 = __builtin_amdgcn_readfirstlane(ni * BN_OUT);
     const int miu = __builtin_amdgcn_readfirstlane(mi);
+    // small tiles stream weights and gain nothing from the product tables (their
+    // VALU work hides behind the loads), so only 128-row tiles use them
+    using P1 = std::integral_constant<bool, true>;
+    using P0 = std::integral_constant<bool, false>;
     if (rows <= BMS)
-      run_tile(std::integral_constant<int, BMS>{}, gu, r0 + miu * BMS, r0 + rows, n0);
+      run_tile(std::integral_constant<int, BMS>{}, P0{}, gu, r0 + miu * BMS, r0 + rows, n0);
+    else if (KB <= PT_KB)
+      run_tile(std::integral_constant<int, BMB>{}, P1{}, gu, r0 + miu * BMB, r0 + rows, n0);
     else
-      run_tile(std::integral_constant<int, BMB>{}, gu, r0 + miu * BMB, r0 + rows, n0);
+      run_tile(std::integral_constant<int, BMB>{}, P0{}, gu, r0 + miu * BMB, r0 + rows, n0);
   }
 }
 

@@ -412,6 +412,38 @@ def test_grouped_gemm_fp8_limits(case):
             _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
 
 
+@pytest.mark.parametrize("K", [8192, 8320])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_fp8_scale_table_forms(K, swiglu):
+    """Both sides of the K at which 128-row tiles stop keeping row-scale x weight-scale
+    products in LDS (64 blocks) and form the products in the K loop: mixed 32- and
+    128-row tiles; plain N = 384 ends on a half column tile (one weight-scale block)."""
+    sizes, m_align = [150, 20, 260, 0, 7], 16
+    N = 256 if swiglu else 384
+    note(f"gemm fp8 table forms K={K} swiglu={swiglu}")
+    a, b, offsets, R = _gemm_case(sizes, N, K, m_align, 53, swiglu)
+    qa, sa = M.moe_quant_fp8(a.to(dev()))
+    qb, sb = M.moe_quant_weight_fp8(b.to(dev()))
+    qao, sao = OC.quant_fp8_act(a.numpy())
+    qbo, sbo = OC.quant_fp8_weight(b.numpy())
+    off_d = torch.from_numpy(offsets).to(dev())
+    ref = O.grouped_gemm_fp8(qao, sao, qbo, sbo, offsets)
+    live = np.zeros(R, bool)
+    for g in range(len(sizes)):
+        live[offsets[g]:offsets[g] + sizes[g]] = True
+    if not swiglu:
+        c = M.grouped_gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb), sb, off_d, R, N)
+        beyond, raw = error_ratios(to_np(c)[live], ref[live])
+        assert beyond <= TOL, beyond
+    else:
+        codes, sc = M.grouped_gemm_fp8(qa, sa, M.moe_pack_weight_fp8(qb), sb, off_d, R, N,
+                                       swiglu=True)
+        A = OC.dequant_fp8_act(qao, sao)
+        Bd = OC.dequant_fp8_weight(qbo, sbo)
+        sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)
+        _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
+
+
 @pytest.mark.parametrize("Mrows,K", [(0, 512), (1, 512), (200, 512), (333, 512),
                                      (333, 128), (40, 256), (333, 640)])
 def test_gemm_fp8_dense(Mrows, K):
