@@ -117,7 +117,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
   constexpr int A_STAGE = BMB * 128;               // activation codes of one K block
   constexpr int NSA = 4;                           // activation stage arrays
   constexpr int TAB_FLOATS = kGemmMaxKBlocks * BMB;
-  constexpr int OUT_FLOATS = SWIGLU ? BMB * 132 : BMB * 128;
+  constexpr int OUT_FLOATS = BMB * 132;             // epilogue rows of 528 bytes
   __shared__ TileMap tm;
   // four activation stages, each an LDS object of its own (see dma16b); the row-scale
   // table [kb][row] doubles as the epilogue's staging area
@@ -341,9 +341,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     static_assert((UNR * TM) % AR == 0 && (UNR * TM) % PR == 0 && (UNR * TM) % SR == 0,
                   "ring phases");
     v8i af[AR];
-    v4f sa[SR][NSC];
+    float sa[SR][NSC];
     v4f pp[PR][TN];
-    v4f cq[PROD ? 1 : PR][2];
+    float cq[PROD ? 1 : PR][2];
     // plain PROD: the table of this wave's half
     const float* tabw = tab + ((PROD && !SWIGLU && wcol >= 128) ? PT_KB * BMB : 0);
     auto rd_a = [&](const uint8_t* L, int i) {
@@ -353,9 +353,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       const v4i hi = *reinterpret_cast<const v4i*>(base + (((gsel + 1) ^ swz(row)) << 4));
       return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
+    // the scale of this lane's output row (see the MFMA operand order below)
     auto rd_s = [&](int kbx, int i, int t = 0) {
-      return *reinterpret_cast<const v4f*>(tabw + (t * PT_KB + kbx) * BMB + i * 16 +
-                                           (lane >> 4) * 4);
+      return tabw[(t * PT_KB + kbx) * BMB + i * 16 + (lane & 15)];
     };
     auto rd_sets = [&](int sslot, int kbx, int i) {
 #pragma unroll
@@ -366,11 +366,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int h = (SWIGLU && j >= TN / 2) ? 1 : 0;
-        v4f c;
+        float c;
         if constexpr (PROD) c = sa[sslot][NSC > 1 ? h : 0];
         else c = cq[slot][h];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[ii][j][r] = fmaf(c[r], pp[slot][j][r], acc[ii][j][r]);
+        for (int r = 0; r < 4; ++r) acc[ii][j][r] = fmaf(c, pp[slot][j][r], acc[ii][j][r]);
       }
     };
 
@@ -411,10 +411,12 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
             rd_sets(sslot, min(kb + 1, KB - 1), ni - TM);
           }
         }
+        // weights as the A operand, activations as B: the 16x16 partial is the transposed
+        // tile, each lane holding four consecutive output columns of one output row
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           pp[gs % PR][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[gs % AR], bq[ub][j], zero, 0, 0, 0, 0, 0, 0);
+              bq[ub][j], af[gs % AR], zero, 0, 0, 0, 0, 0, 0);
         if constexpr (!PROD) {
           cq[gs % PR][0] = sa[gs % SR][0] * sbA;
           cq[gs % PR][1] = sa[gs % SR][0] * sbB;
@@ -454,11 +456,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
 #pragma unroll
     for (int i = RA; i < SR; ++i)
 #pragma unroll
-      for (int t = 0; t < NSC; ++t) sa[i][t] = zero;
+      for (int t = 0; t < NSC; ++t) sa[i][t] = 0.f;
 #pragma unroll
     for (int p = 0; p < (PROD ? 1 : PR); ++p) {
-      cq[p][0] = zero;
-      cq[p][1] = zero;
+      cq[p][0] = 0.f;
+      cq[p][1] = 0.f;
     }
 #pragma unroll
     for (int p = 0; p < PR; ++p)
@@ -496,22 +498,26 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     wait_vmcnt<0>();  // the last (clamped) activation DMAs land before LDS is reused
     lds_barrier();
 
-    // ---- epilogue.  MFMA C layout: lane holds column lane%16, rows 4*(lane/16)+r.
+    // ---- epilogue.  acc[i][j] of a lane: tile row i*16 + lane%16, columns
+    // j*16 + 4*(lane/16) + r of the wave's slice (the transposed MFMA tile).
     if constexpr (!SWIGLU) {
-      // bf16 tile staged through LDS for 16-byte stores
-      constexpr int OB = 512;
+      // bf16 tile staged through LDS for 16-byte stores; rows of 528 bytes put the 16
+      // rows of one 8-byte write in different banks
+      constexpr int OB = 528;
       uint8_t* ot = reinterpret_cast<uint8_t*>(tab);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        const int trow = i * 16 + (lane & 15);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int trow = i * 16 + (lane >> 4) * 4 + r;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const int tcol = wid * WB + j * 16 + (lane & 15);
-            *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(acc[i][j][r]);
-          }
+        for (int j = 0; j < TN; ++j) {
+          const int tcol = wid * WB + j * 16 + (lane >> 4) * 4;
+          const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][0]) |
+                              ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][j][2]) |
+                              ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(ot + trow * OB + tcol * 2) = make_uint2(lo, hi);
         }
+      }
       __syncthreads();
       uint8_t* C = static_cast<uint8_t*>(args.C);
       const int cpr = ncols * 2 / 16;              // 16-byte chunks per valid row
@@ -526,13 +532,14 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       constexpr int HS = 132;
       float* hsm = tab;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        const int trow = i * 16 + (lane & 15);
+        const int tcol = wid * WB + (lane >> 4) * 4;
+        v4f h;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int trow = i * 16 + (lane >> 4) * 4 + r;
-          const int tcol = wid * WB + (lane & 15);
-          hsm[trow * HS + tcol] = silu_fast(acc[i][0][r]) * acc[i][1][r];
-        }
+        for (int r = 0; r < 4; ++r) h[r] = silu_fast(acc[i][0][r]) * acc[i][1][r];
+        *reinterpret_cast<v4f*>(hsm + trow * HS + tcol) = h;
+      }
       __syncthreads();
       const int row = tid >> 2, part = tid & 3;
       float hv[32];
