@@ -116,7 +116,10 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
   constexpr int WB = (SWIGLU ? 128 : 256) / NW;    // weight rows per wave (per half: SwiGLU)
   constexpr int A_STAGE = BMB * 128;               // activation codes of one K block
   constexpr int NSA = 4;                           // activation stage arrays
-  constexpr int TAB_FLOATS = kGemmMaxKBlocks * BMB;
+  // scale table [kb][row], rows of TS floats: the 4-float pad puts the four 16-row
+  // groups one fill instruction writes (four consecutive K-block quads) in different banks
+  constexpr int TS = BMB + 4;
+  constexpr int TAB_FLOATS = kGemmMaxKBlocks * TS;
   constexpr int OUT_FLOATS = BMB * 132;             // epilogue rows of 528 bytes
   __shared__ TileMap tm;
   // four activation stages, each an LDS object of its own (see dma16b); the row-scale
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
   __shared__ __attribute__((aligned(1024))) float tab[TAB_FLOATS > OUT_FLOATS ? TAB_FLOATS : OUT_FLOATS];
   __shared__ int row_src[BMB];
   // product tables: the tile's two weight-scale rows, table t at [t * PT_KB + kb]
-  constexpr int PT_KB = TAB_FLOATS / (2 * BMB);
+  constexpr int PT_KB = TAB_FLOATS / (2 * TS);
   __shared__ float sbt[2 * PT_KB];
   auto stage = [&](auto S) -> uint8_t* {
     constexpr int sidx = decltype(S)::value % NSA;
@@ -230,24 +233,25 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     // round before its LDS writes, so the latency is paid once per round.
     {
       constexpr int TAB_IT = 4;                    // items per thread per round
+      constexpr int RSTEP = NT / 16;               // item quads between a thread's items
       const int nq = (KB + 3) / 4;
       const int tab_items = BM * nq;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(args.sA), (short)0, -1, 0x00020000);
-      auto item = [&](int p, int& row, int& q) {
-        const int rest = p >> 4;
-        q = rest % nq;
-        row = (rest / nq) * 16 + (p & 15);
-      };
+      // item p: row group rb = (p / 16) / nq, quad q = (p / 16) % nq, row rb*16 + p%16.
+      // A thread's items are RSTEP apart in p / 16: (rb, q) advance by a fixed step.
+      const int drb = RSTEP / nq, dq = RSTEP - drb * nq;
+      int rb = (tid >> 4) / nq, q = (tid >> 4) - rb * nq;
+      const int rlo = tid & 15;
       for (int p0 = 0; p0 < tab_items; p0 += TAB_IT * NT) {
         v4i tv[TAB_IT];
+        int rowv[TAB_IT], qv[TAB_IT];
 #pragma unroll
         for (int it = 0; it < TAB_IT; ++it) {
-          const int p = p0 + tid + it * NT;
-          if (p < tab_items) {
-            int row, q;
-            item(p, row, q);
-            const uint32_t base = (uint32_t)row_src[row] * (uint32_t)KB;
+          rowv[it] = rb * 16 + rlo;
+          qv[it] = q;
+          if (p0 + tid + it * NT < tab_items) {
+            const uint32_t base = (uint32_t)row_src[rowv[it]] * (uint32_t)KB;
             if (4 * q + 3 < KB) {
               tv[it] = __builtin_bit_cast(
                   v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, (base + 4 * q) * 4u, 0, 0));
@@ -258,23 +262,27 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
                     rs, (base + (uint32_t)min(4 * q + t, KB - 1)) * 4u, 0, 0);
             }
           }
+          rb += drb;
+          q += dq;
+          if (q >= nq) {
+            q -= nq;
+            ++rb;
+          }
         }
 #pragma unroll
         for (int it = 0; it < TAB_IT; ++it) {
-          const int p = p0 + tid + it * NT;
-          if (p < tab_items) {
-            int row, q;
-            item(p, row, q);
+          if (p0 + tid + it * NT < tab_items) {
+            const int row = rowv[it];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              const int kb = 4 * q + t;
+              const int kb = 4 * qv[it] + t;
               if (kb < KB) {
                 const float a = __int_as_float(tv[it][t]);
                 if constexpr (PROD) {
-                  tab[kb * BMB + row] = a * sbt[kb];
-                  tab[(PT_KB + kb) * BMB + row] = a * sbt[PT_KB + kb];
+                  tab[kb * TS + row] = a * sbt[kb];
+                  tab[(PT_KB + kb) * TS + row] = a * sbt[PT_KB + kb];
                 } else {
-                  tab[kb * BMB + row] = a;
+                  tab[kb * TS + row] = a;
                 }
               }
             }
@@ -345,7 +353,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     v4f pp[PR][TN];
     float cq[PROD ? 1 : PR][2];
     // plain PROD: the table of this wave's half
-    const float* tabw = tab + ((PROD && !SWIGLU && wcol >= 128) ? PT_KB * BMB : 0);
+    const float* tabw = tab + ((PROD && !SWIGLU && wcol >= 128) ? PT_KB * TS : 0);
     auto rd_a = [&](const uint8_t* L, int i) {
       const int row = i * 16 + (lane & 15);
       const uint8_t* base = L + row * 128;
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     };
     // the scale of this lane's output row (see the MFMA operand order below)
     auto rd_s = [&](int kbx, int i, int t = 0) {
-      return tabw[(t * PT_KB + kbx) * BMB + i * 16 + (lane & 15)];
+      return tabw[(t * PT_KB + kbx) * TS + i * 16 + (lane & 15)];
     };
     auto rd_sets = [&](int sslot, int kbx, int i) {
 #pragma unroll
@@ -520,11 +528,29 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       }
       __syncthreads();
       uint8_t* C = static_cast<uint8_t*>(args.C);
-      const int cpr = ncols * 2 / 16;              // 16-byte chunks per valid row
-      for (int c = tid; c < n_valid * cpr; c += NT) {
-        const int trow = c / cpr, ch = c % cpr;
-        *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) =
-            *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
+      if (ncols == BN_OUT) {
+        // full tile: thread tid takes 16-byte chunk tid % 32 of rows tid / 32 + 16 k; all
+        // LDS reads go out before the stores
+        constexpr int CPR = BN_OUT * 2 / 16, RPP = NT / CPR;
+        static_assert(BM % RPP == 0, "store passes");
+        const int ch = tid % CPR, tr0 = tid / CPR;
+        v4i ov[BM / RPP];
+#pragma unroll
+        for (int k = 0; k < BM / RPP; ++k)
+          ov[k] = *reinterpret_cast<const v4i*>(ot + (tr0 + k * RPP) * OB + ch * 16);
+#pragma unroll
+        for (int k = 0; k < BM / RPP; ++k) {
+          const int trow = tr0 + k * RPP;
+          if (trow < n_valid)
+            *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) = ov[k];
+        }
+      } else {
+        const int cpr = ncols * 2 / 16;            // 16-byte chunks per valid row
+        for (int c = tid; c < n_valid * cpr; c += NT) {
+          const int trow = c / cpr, ch = c % cpr;
+          *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) =
+              *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
+        }
       }
     } else {
       // h = silu(gate) * up goes to LDS in fp32 (row stride 132 floats); then four
