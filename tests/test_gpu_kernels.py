@@ -509,12 +509,19 @@ def test_grouped_gemm_f32(swiglu):
     assert raw <= TOL
 
 
+@pytest.mark.parametrize("T,k,E,cap", [
+    (99, 4, 16, 20),      # some slots dropped
+    (64, 10, 32, 3),      # two load batches of slots; tokens with every slot dropped
+    (50, 1, 8, 0),        # one slot per token, no capacity limit
+])
 @pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32])
-def test_combine(o_dtype):
-    note(f"combine {o_dtype}")
-    T, k, E, d = 99, 4, 16, 256
+def test_combine(o_dtype, T, k, E, cap):
+    note(f"combine {o_dtype} T={T} k={k} E={E} cap={cap}")
+    d = 256
     idx = synth.random_topk(T, E, k, seed=5)
-    _, offsets, ros, sor = O.dispatch(idx, E, 8, cap=20)
+    _, offsets, ros, sor = O.dispatch(idx, E, 8, cap=cap)
+    if cap == 3:
+        assert np.any(np.all(ros.reshape(T, k) < 0, axis=1)), "no fully dropped token"
     R = len(sor)
     o = synth.normal((R, d), 14, "x", dtype=o_dtype)
     w = synth.uniform((T, k), 0, 1, 14, "bias")
