@@ -32,7 +32,7 @@
 //     tile, so that the K loop loads no scattered scale words.
 //   * Persistent grid; workgroup b works on tiles v, v+P, ... with v = (b mod 8) * P/8 +
 //     b/8, so that the 32 tiles one XCD holds at a time are consecutive; inside a group
-//     they run down up to 8 row tiles before moving to the next column tile, so those
+//     they run down up to 16 row tiles before moving to the next column tile, so those
 //     tiles share a few activation row tiles and weight column tiles in that XCD's L2.
 //     The tiles of large groups (MFMA-bound) and of small groups (bound by the weight
 //     stream) are interleaved by XCD-sized windows in proportion to their counts, so
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
   for (int t = v; t < nq * Q; t += P) {
     // ---- locate the tile: within a group, runs of up to GM row tiles are walked column
     // tile by column tile
-    constexpr int GM = 8;
+    constexpr int GM = 16;
     // window tb holds large-group tiles if floor(tb nbq / nq) steps at tb; slots past
     // the end of a list hold no tile
     const int tb = t / Q, to = t - tb * Q;
