@@ -13,7 +13,9 @@
 // gfx950 mapping
 //   * v_mfma_f32_16x16x128_f8f6f4: one instruction covers one 16x16 output tile over
 //     exactly one 128-deep scale block, so promotion is one fp32 FMA per output per
-//     block: acc += (sA*sB) * mfma(a, b, 0).
+//     block: acc += (sA*sB) * mfma(b, a, 0).  With the weight fragment as the A operand
+//     the partial is the transposed tile, so a lane's four values share one output row
+//     (one row scale per step) and are four consecutive columns (wide epilogue stores).
 //   * 512 threads = 8 wave64s, two per SIMD: the promotion arithmetic of one wave runs
 //     while the other wave's MFMAs occupy the matrix core.  A workgroup tile is BM rows x
 //     256 weight rows (plain: 256 output columns; SwiGLU: 128 gate + 128 up rows, so the
@@ -29,7 +31,9 @@
 //     of those last steps already fetch the next block's first fragments, so the MFMAs
 //     never wait on the barrier.
 //   * The tile's activation scales for all K blocks are transposed into LDS once per
-//     tile, so that the K loop loads no scattered scale words.
+//     tile, so that the K loop loads no scattered scale words; for 128-row tiles with
+//     K <= 8192 the table holds the products sA*sB (one table per weight-scale block of
+//     the tile), so the promotion needs no multiply in the K loop.
 //   * Persistent grid; workgroup b works on tiles v, v+P, ... with v = (b mod 8) * P/8 +
 //     b/8, so that the 32 tiles one XCD holds at a time are consecutive; inside a group
 //     they run down up to 16 row tiles before moving to the next column tile, so those
