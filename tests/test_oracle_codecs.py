@@ -164,3 +164,50 @@ def test_fp4_bytes_example(golden):
     n = ex["shape"][0] * ex["shape"][1]
     assert round(n * 2 / 2 ** 20) == ex["fp16_MiB"]
     assert round(n * 0.5 / 2 ** 20) == ex["fp4_MiB"]
+
+
+def _int4_dequant_by_torch(q, s7):
+    """bf16(fl32(q * s7)) with torch's fp32 product and torch's own RNE bf16 cast."""
+    qt = torch.from_numpy(np.asarray(q, np.int8).astype(np.float32))
+    G, N, K = qt.shape
+    st = torch.from_numpy(np.asarray(s7, np.float32)).repeat_interleave(128, dim=2)
+    return (qt * st).to(torch.bfloat16).to(torch.float32).numpy().reshape(G, N, K)
+
+
+def test_int4_dequant_exact_every_code():
+    """Exact pin of the dequantised int4 weight bf16(fl32(q * s7)) (tqpw.cn sec. 3.1, read
+    as the bf16 value the matrix product consumes): every code -7..7 against a sweep of
+    stored scales (random mantissas over many binades, powers of two, values whose
+    products sit on bf16 rounding ties), compared bit for bit with torch's casts."""
+    rng = np.random.default_rng(23)
+    codes = np.tile(np.arange(-7, 8, dtype=np.int8), 9)[:128]
+    s = np.concatenate([
+        rng.uniform(1.0, 2.0, 300) * np.exp2(rng.integers(-30, 10, 300)),
+        np.exp2(np.arange(-20, 5, dtype=np.float64)),
+        1.0 + np.arange(1, 64) * 2.0 ** -8,          # q * s7 lands on bf16 ties for odd q
+        (1.0 + 2.0 ** -7) / 3.0 * np.ones(4),
+    ]).astype(np.float32)
+    q = np.broadcast_to(codes, (len(s), 128))[None].copy()
+    s7 = s[None, :, None]
+    got = C.int4_dequant(q, s7)
+    want = _int4_dequant_by_torch(q, s7)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    # a different rounding order (bf16 scale times code) disagrees on this sweep
+    alt = (torch.from_numpy(s).to(torch.bfloat16).float()[:, None] *
+           torch.from_numpy(codes.astype(np.float32))[None, :]).numpy()[None]
+    assert np.any(alt != want)
+
+
+def test_int4_quant_dequant_roundtrip_exact_codes():
+    """Weights that are exact multiples of their block's s7 survive quantisation: the codes
+    come back unchanged and the dequantised weight is bf16 of that multiple."""
+    rng = np.random.default_rng(29)
+    q0 = rng.integers(-7, 8, (2, 3, 256)).astype(np.int8)
+    q0[:, :, 5] = 7                               # every block holds its maximum code
+    q0[:, :, 133] = -7
+    s7 = np.float32(2.0 ** -5)
+    w = q0.astype(np.float32) * s7                # exact in fp32
+    q, s7o = C.int4_quant_rows(w)
+    np.testing.assert_array_equal(q, q0)
+    assert np.all(s7o == s7)
+    np.testing.assert_array_equal(C.int4_dequant(q, s7o), w)

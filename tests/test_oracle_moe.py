@@ -292,3 +292,92 @@ def test_layer_fp8_matches_dequantised_fp32_layer():
             hd = (hq * s.double()[:, :, None]).view(I)
             y[t] += out["w"][t, j] * (W2[e] @ hd)
     np.testing.assert_allclose(out["y"], y.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ combine
+
+def _combine_sparse(o, ros, w, T, k):
+    """y = S o with S [T, rows] the sparse gate matrix, S[t, row(t, j)] = w[t, j] for
+    kept slots: the combine written as one sparse-dense product (scipy), a different
+    route from the oracle's per-slot loop."""
+    import scipy.sparse as sp
+    ros = np.asarray(ros).reshape(T * k)
+    w = np.asarray(w, np.float64).reshape(T * k)
+    keep = ros >= 0
+    tok = np.repeat(np.arange(T), k)[keep]
+    S = sp.csr_matrix((w[keep], (tok, ros[keep])), shape=(T, o.shape[0]))
+    return np.asarray(S @ np.asarray(o, np.float64))
+
+
+def _combine_pins_hold(fn) -> bool:
+    """Whether a combine implementation ``fn(o, row_of_slot, w, T, k)`` meets every pin:
+    the worked integer example, and agreement with the sparse product on random cases
+    with dropped slots, k = 1 and k = E (y = sum over the top-k of G(x)_i E_i(x),
+    discosf.com sec. 2.1)."""
+    # worked example: T = 3 tokens, k = 2, d = 3; dyadic weights, so every sum is exact.
+    # token 0 -> rows 2 (w 0.5) and 0 (w 0.25); token 1 -> row 1 (w 1), slot 1 dropped;
+    # token 2 -> both slots dropped.
+    o = np.array([[4.0, -8.0, 12.0], [1.0, 2.0, 3.0], [-2.0, 6.0, 10.0], [100.0, 100.0, 100.0]])
+    ros = np.array([2, 0, 1, -1, -1, -1], np.int32)
+    w = np.array([[0.5, 0.25], [1.0, 0.5], [0.75, 0.125]])
+    want = np.array([[-1.0 + 1.0, 3.0 - 2.0, 5.0 + 3.0],   # 0.5*row2 + 0.25*row0
+                     [1.0, 2.0, 3.0],
+                     [0.0, 0.0, 0.0]])
+    try:
+        if not np.array_equal(fn(o, ros, w, 3, 2), want):
+            return False
+        rng = np.random.default_rng(17)
+        for T, k, E, cap in ((13, 3, 5, 6), (9, 1, 4, 0), (7, 4, 4, 0), (11, 2, 3, 2)):
+            idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+            _, offsets, r, sor = O.dispatch(idx, E, 4, cap)
+            oo = rng.standard_normal((len(sor), 6))
+            ww = rng.uniform(0.1, 1.0, (T, k))
+            got = fn(oo, r, ww, T, k)
+            if got.shape != (T, 6) or not np.allclose(got, _combine_sparse(oo, r, ww, T, k),
+                                                      rtol=1e-13, atol=1e-13):
+                return False
+    except (IndexError, ValueError):
+        return False
+    return True
+
+
+def test_combine_pins():
+    assert _combine_pins_hold(O.combine)
+
+
+def test_combine_pins_catch_planted_mistakes():
+    """Each plausible slip in a combine (transposed slot order, weights read by the wrong
+    index, a dropped slot's -1 used as a row) fails the pins above."""
+    def transposed_slots(o, ros, w, T, k):
+        return O.combine(o, np.asarray(ros).reshape(k, T).T.ravel(), w, T, k)
+
+    def weight_index(o, ros, w, T, k):
+        return O.combine(o, ros, np.asarray(w).reshape(T, k)[:, ::-1], T, k)
+
+    def drop_as_row(o, ros, w, T, k):
+        o = np.asarray(o, np.float64)
+        r = np.asarray(ros).reshape(T, k)
+        wk = np.asarray(w, np.float64).reshape(T, k)
+        return sum(wk[:, j:j + 1] * o[r[:, j]] for j in range(k))
+
+    for bad in (transposed_slots, weight_index, drop_as_row):
+        assert not _combine_pins_hold(bad), bad.__name__
+
+
+def test_layer_output_is_combine_of_expert_rows():
+    """layer_forward's y equals oracle.combine over its own expert rows, so the layer's
+    weighted sum and the pinned combine are one operation."""
+    T, d, E, k, I = 24, 128, 6, 3, 64
+    x = synth.normal((T, d), 4, "x").numpy()
+    wr = synth.normal((E, d), 4, "w_gate_router", std=d ** -0.5).numpy()
+    b = synth.uniform((E,), -0.01, 0.01, 4, "bias").numpy()
+    w13, w2 = _fp32_experts(E, d, I, 4)
+    out = O.layer_forward("fp32", x, E=E, k=k, I=I, w_router=wr, bias=b, experts=(w13, w2),
+                          m_align=4, cap_factor=1.0)
+    ros = out["row_of_slot"]
+    assert np.any(ros < 0)                       # the capacity dropped some slots
+    o_rows = np.zeros((len(out["slot_of_row"]), d))
+    for s, v in out["o_by_slot"].items():
+        o_rows[ros[s]] = v
+    np.testing.assert_allclose(out["y"], O.combine(o_rows, ros, out["w"], T, k),
+                               rtol=1e-14, atol=1e-14)
