@@ -69,15 +69,20 @@ int hip_status(hipError_t e, const char* what) {
 
 inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
-// Rows per small-group GEMM tile from the average rows per group: decode-sized groups
-// use 16-row tiles, everything else 32-row tiles (measured best at the prefill shape,
-// where most groups hold about 20 rows); groups above it use 128-row tiles.
-int pick_bm(double avg_rows, bool swiglu) {
-  (void)swiglu;
-  return avg_rows <= 16 ? 16 : 32;
-}
+// Rows per small-group GEMM tile from the rows an entry point is given per group
+// (R_cap / G, which includes each group's padding up to m_align - 1 rows): decode-sized
+// groups (at most 32 rows per group, i.e. about 16 live rows at m_align = 16) use
+// 16-row tiles, everything else 32-row tiles (measured best at the prefill shape, where
+// most groups hold about 20 rows); groups above the small-tile size use 128-row tiles.
+// The layer applies the same rule to its own rows bound, so the layer and the entry
+// point pick the same kernel for the same problem.
+int pick_bm(double rows_per_group) { return rows_per_group <= 32 ? 16 : 32; }
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+// The FP8 GEMM addresses its activation operand through a buffer resource with 32-bit
+// byte offsets (row * K): every row it reads must end below this bound.
+constexpr long long kMaxOperandBytes = (1LL << 32) - 256;
 
 // ------------------------------------------------------------ pure validation
 int v_route_from_logits(const void* logits, int T, int E, int k, unsigned flags, const void* idx,
@@ -286,13 +291,16 @@ int grouped_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows, i
   } else {
     REQUIRE(out_dt == MOE_BF16, "grouped_gemm_fp8: plain epilogue writes bf16");
   }
+  REQUIRE(a_rows || (long long)R_cap * K <= kMaxOperandBytes,
+          "grouped_gemm_fp8: R_cap * K = %lld exceeds the 32-bit operand offset range",
+          (long long)R_cap * K);
   if ((st = v_fp8_out_vs_scales("grouped_gemm_fp8", sB, G, swiglu ? 2 * N : N, K, C, sC, R_cap,
                                 N, swiglu)))
     return st;
   if (R_cap == 0) return MOE_OK;
   int cus = 0;
   if ((st = current_device(&cus))) return st;
-  const int bm = pick_bm((double)R_cap / G, swiglu);
+  const int bm = pick_bm((double)R_cap / G);
   return hip_status(moe::launch_gemm_fp8(A, sA, a_rows, a_row_div, B, sB, offsets, G, R_cap, N, K,
                                          swiglu, C, sC, bm, cus, S(stream)),
                     "grouped_gemm_fp8 launch");
@@ -317,6 +325,9 @@ int grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B,
   } else {
     REQUIRE(out_dt == MOE_BF16, "grouped_gemm_fp8_masked: plain epilogue writes bf16");
   }
+  REQUIRE((long long)rows * K <= kMaxOperandBytes,
+          "grouped_gemm_fp8_masked: G * cap * K = %lld exceeds the 32-bit operand offset range",
+          (long long)rows * K);
   if ((st = v_fp8_out_vs_scales("grouped_gemm_fp8_masked", sB, G, swiglu ? 2 * N : N, K, C, sC,
                                 rows, N, swiglu)))
     return st;
@@ -324,7 +335,7 @@ int grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B,
   int cus = 0;
   if ((st = current_device(&cus))) return st;
   return hip_status(moe::launch_gemm_fp8(A, sA, nullptr, 1, B, sB, counts, G, rows, N, K, swiglu,
-                                         C, sC, pick_bm(cap, swiglu), cus, S(stream),
+                                         C, sC, pick_bm(cap), cus, S(stream),
                                          moe::kRowsMasked, cap),
                     "grouped_gemm_fp8_masked launch");
 }
@@ -336,6 +347,8 @@ int gemm_fp8(const uint8_t* A, const float* sA, const uint8_t* B, const float* s
   REQUIRE(N % 128 == 0 && K % 128 == 0, "gemm_fp8: N and K must be multiples of 128");
   REQUIRE(K / 128 <= moe::kGemmMaxKBlocks, "gemm_fp8: K must be <= %d",
           128 * moe::kGemmMaxKBlocks);
+  REQUIRE((long long)M * K <= kMaxOperandBytes,
+          "gemm_fp8: M * K = %lld exceeds the 32-bit operand offset range", (long long)M * K);
   int st = v_fp8_out_vs_scales("gemm_fp8", sB, 1, N, K, C, nullptr, M, N, false);
   if (st) return st;
   if (M == 0) return MOE_OK;
@@ -343,7 +356,7 @@ int gemm_fp8(const uint8_t* A, const float* sA, const uint8_t* B, const float* s
   st = current_device(&cus);
   if (st) return st;
   return hip_status(moe::launch_gemm_fp8(A, sA, nullptr, 1, B, sB, nullptr, 1, M, N, K, false, C,
-                                         nullptr, pick_bm(M, false), cus, S(stream),
+                                         nullptr, pick_bm(M), cus, S(stream),
                                          moe::kRowsDense, M),
                     "gemm_fp8 launch");
 }
@@ -419,6 +432,13 @@ int layer_check(const moe_layer_desc* d) {
     REQUIRE(d->I % 128 == 0, "moe_layer: fp8 needs I %% 128 == 0");
     REQUIRE(d->d <= 128 * moe::kGemmMaxKBlocks && d->I <= 128 * moe::kGemmMaxKBlocks,
             "moe_layer: fp8 needs d, I <= %d", 128 * moe::kGemmMaxKBlocks);
+  }
+  if (d->mode == MOE_MODE_FP8) {
+    // GEMM1 reads the token codes [T, d], GEMM2 the h codes [R, I] with 32-bit offsets
+    const long long R = (long long)d->T * d->k + (long long)d->E * (d->m_align - 1);
+    REQUIRE((long long)d->T * d->d <= kMaxOperandBytes && R * d->I <= kMaxOperandBytes,
+            "moe_layer: fp8 operands T*d = %lld or rows*I = %lld exceed the 32-bit offset range",
+            (long long)d->T * d->d, R * d->I);
   }
   if (d->mode == MOE_MODE_W4A16) REQUIRE(d->I % 128 == 0, "moe_layer: w4a16 needs I %% 128 == 0");
   if (d->mode == MOE_MODE_FP32) REQUIRE(d->I % 16 == 0, "moe_layer: fp32 needs I %% 16 == 0");
@@ -516,7 +536,7 @@ int moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* w, const voi
   if (cap < 0) return cap;
   STEP(moe::launch_dispatch(idx, T, k, E, d->m_align, cap, counts, offsets, ros, sor, R, s),
        "dispatch launch");
-  const double avg = (double)T * k / E;
+  const double rows_per_group = (double)R / E;
   void* o = base + L.o;
   if (d->mode == MOE_MODE_FP8) {
     uint8_t* qx = base + L.qx;
@@ -525,10 +545,11 @@ int moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* w, const voi
     float* sh = reinterpret_cast<float*>(base + L.sh);
     STEP(moe::launch_quant_act(x, true, D, nullptr, 1, T, qx, sx, s), "quant launch");
     STEP(moe::launch_gemm_fp8(qx, sx, sor, k, static_cast<const uint8_t*>(w->w13), w->s13, offsets,
-                              E, R, I, D, true, hq, sh, pick_bm(avg, true), cus, s),
+                              E, R, I, D, true, hq, sh, pick_bm(rows_per_group), cus, s),
          "gemm1 launch");
     STEP(moe::launch_gemm_fp8(hq, sh, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
-                              offsets, E, R, D, I, false, o, nullptr, pick_bm(avg, false), cus, s),
+                              offsets, E, R, D, I, false, o, nullptr, pick_bm(rows_per_group),
+                              cus, s),
          "gemm2 launch");
   } else if (d->mode == MOE_MODE_W4A16) {
     uint16_t* h = reinterpret_cast<uint16_t*>(base + L.h);

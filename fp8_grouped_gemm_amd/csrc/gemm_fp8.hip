@@ -601,13 +601,14 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       m = fmaxf(m, __shfl_xor(m, 1, 64));
       m = fmaxf(m, __shfl_xor(m, 2, 64));
       if (row < n_valid) {
+        // the activation quantiser's rule: s = fl32(amax / 448), q = e4m3(fl32(h / s)),
+        // with correctly rounded divisions (not a multiply by a rounded reciprocal)
         const float sc = block_scale(m);
-        const float inv = 1.0f / sc;
         uint32_t w[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          w[q] = e4m3x4(clamp448(hv[4 * q] * inv), clamp448(hv[4 * q + 1] * inv),
-                        clamp448(hv[4 * q + 2] * inv), clamp448(hv[4 * q + 3] * inv));
+          w[q] = e4m3x4(clamp448(hv[4 * q] / sc), clamp448(hv[4 * q + 1] / sc),
+                        clamp448(hv[4 * q + 2] / sc), clamp448(hv[4 * q + 3] / sc));
         uint8_t* C = static_cast<uint8_t*>(args.C) + (size_t)(row0 + row) * N + n0 + part * 32;
         *reinterpret_cast<v4i*>(C) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
         *reinterpret_cast<v4i*>(C + 16) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};

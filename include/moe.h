@@ -93,8 +93,9 @@ size_t moe_rows_bound(int T, int k, int E, int m_align);
  *   topk_idx [T, k] int32 and topk_w [T, k] fp32 outputs;
  *   ws / ws_bytes: optional device workspace for split-K partial logits; with at least
  *   moe_route_workspace_size() bytes the logit product is split along d over more
- *   workgroups (summed in a fixed order, so results do not depend on it); NULL or
- *   smaller runs unsplit.
+ *   workgroups, whose partial sums are added in a fixed order (deterministic for a
+ *   given shape; the split changes the fp32 summation order, so logits with and
+ *   without a workspace may differ in their last bits); NULL or smaller runs unsplit.
  *   1 <= k <= min(E, 64), E <= 1024; d a multiple of 128 for MOE_BF16. */
 int moe_route(const void *x, moe_dtype x_dt, const void *w_router, const float *bias,
               int T, int d, int E, int k, unsigned flags, float *logits,
@@ -103,9 +104,12 @@ int moe_route(const void *x, moe_dtype x_dt, const void *w_router, const float *
 /* Workspace bytes moe_route uses to split the logit product (0: it never splits). */
 size_t moe_route_workspace_size(int T, int d, int E, moe_dtype x_dt);
 
-/* Top-k of fp32 logits [T, E] with per-expert bias [E] (bias may be NULL = 0).
- * key_e = fl32(logit_e + b_e); the k largest keys are chosen, largest first, equal
- * keys to the lower expert index; topk_w[t, j] = softmax over all E keys at
+/* Top-k of fp32 logits [T, E] with per-expert bias [E] (bias may be NULL = 0): the
+ * selection and gate weights of s_i = softmax(W_g x + b_i) (MegaMoE walkthrough,
+ * discosf.com, sec. 2.1-2.2; fp32 softmax, DeepSeek-V4 lecture, tqpw.cn, sec. 2.3;
+ * the renormalised variant is the top-k-then-softmax code of DeepSeek MoE
+ * architecture, mooersco.com, ch. 1).  key_e = fl32(logit_e + b_e); the k largest
+ * keys are chosen, largest first, equal keys to the lower expert index; topk_w[t, j] = softmax over all E keys at
  * topk_idx[t, j] (or, with MOE_ROUTE_RENORM, divided by the sum of the k chosen).
  * Logits must be finite.  1 <= k <= min(E, 64), E <= 1024. */
 int moe_route_from_logits(const float *logits, const float *bias, int T, int E, int k,
@@ -178,6 +182,9 @@ int moe_quant_weight_int4(const float *w, int G, int N, int K, uint8_t *q, float
  *     quantised 1x128 as moe_quant_fp8, sC [R_cap, N/128] fp32.
  * Rows >= offsets[G] and padding rows are unspecified.  N and K multiples of 128,
  * K <= 16384 (the kernel keeps a tile's activation scales for all K blocks on chip).
+ * A is read with 32-bit byte offsets: every A row the call reads must end within the
+ * first 2^32 - 256 bytes of A (checked as R_cap * K when a_rows is NULL; with a_rows
+ * the caller guarantees it for the rows a_rows names).
  * C and sC must not overlap sB (checked: the kernel reads sB through the scalar cache)
  * nor any other input (not checked). */
 int grouped_gemm_fp8(const uint8_t *A, const float *sA, const int32_t *a_rows, int a_row_div,
@@ -190,7 +197,8 @@ int grouped_gemm_fp8(const uint8_t *A, const float *sA, const int32_t *a_rows, i
  * per-expert capacity of mooersco.com sec. 2.5): group g owns rows [g*cap, g*cap +
  * counts[g]) of A [G*cap, K] (counts on the device, clamped to [0, cap]); sA
  * [G*cap, K/128]; C and sC have G*cap rows, rows past counts[g] in each block are
- * unspecified.  No row gather.  B, sB, epilogue, out_dt and sizes as grouped_gemm_fp8. */
+ * unspecified.  No row gather.  B, sB, epilogue, out_dt and sizes as grouped_gemm_fp8;
+ * G * cap * K <= 2^32 - 256. */
 int grouped_gemm_fp8_masked(const uint8_t *A, const float *sA, const uint8_t *B,
                             const float *sB, const int32_t *counts, int G, int cap, int N,
                             int K, int epilogue, moe_dtype out_dt, void *C, float *sC,
@@ -199,12 +207,14 @@ int grouped_gemm_fp8_masked(const uint8_t *A, const float *sA, const uint8_t *B,
 /* Dense FP8 GEMM with the same block scaling (the dense layout, qidao123.com day 3):
  * C [M, N] bf16 = A [M, K] e4m3 (sA [M, K/128]) times B [N, K] e4m3 (sB [N/128, K/128],
  * codes fragment-major as moe_pack_weight_fp8 with G = 1) transposed, promoted per
- * 128-deep K block.  N and K multiples of 128, K <= 16384, M >= 0 (M = 0: nothing is
- * launched, A, sA and C may be null).  C must not overlap sB (checked) nor A, sA, B. */
+ * 128-deep K block.  N and K multiples of 128, K <= 16384, M * K <= 2^32 - 256,
+ * M >= 0 (M = 0: nothing is launched, A, sA and C may be null).  C must not overlap sB (checked) nor A, sA, B. */
 int gemm_fp8(const uint8_t *A, const float *sA, const uint8_t *B, const float *sB, int M,
              int N, int K, uint16_t *C, void *stream);
 
-/* Grouped GEMM with int4 weights and bf16 activations: B codes [G, Nb, K/2] and
+/* Grouped GEMM with int4 weights and bf16 activations (block-wise 4-bit expert weights
+ * with max-abs scales, DeepSeek-V4 lecture, tqpw.cn, sec. 3.1; groups as in the
+ * MegaMoE walkthrough, discosf.com, sec. 3.2): B codes [G, Nb, K/2] and
  * s7 [G, Nb, K/128] are dequantised in-kernel to bf16(fl32(q * s7)) and multiplied with
  * A [*, K] bf16 in fp32.  Row gather and epilogues as grouped_gemm_fp8; output C
  * [R_cap, N] bf16.  N and K multiples of 128. */
@@ -212,7 +222,9 @@ int grouped_gemm_w4a16(const uint16_t *A, const int32_t *a_rows, int a_row_div,
                        const uint8_t *B, const float *s7, const int32_t *offsets, int G,
                        int R_cap, int N, int K, int epilogue, uint16_t *C, void *stream);
 
-/* Grouped fp32 GEMM (no quantisation): A [*, K] fp32, B [G, Nb, K] fp32, C [R_cap, N]
+/* Grouped fp32 GEMM (no quantisation; groups differ in M and share N and K, MegaMoE
+ * walkthrough, discosf.com, sec. 3.2, written as a loop of per-expert GEMMs in the
+ * Dense-to-TP-MoE article, cf-1.com, sec. 4.2): A [*, K] fp32, B [G, Nb, K] fp32, C [R_cap, N]
  * fp32.  Row gather and epilogues as grouped_gemm_fp8.  N multiple of 16, K >= 1. */
 int grouped_gemm_f32(const float *A, const int32_t *a_rows, int a_row_div, const float *B,
                      const int32_t *offsets, int G, int R_cap, int N, int K, int epilogue,
@@ -246,12 +258,17 @@ typedef struct {
   const float *s2;         /* FP8: [E, d/128, I/128]; W4A16: [E, d, I/128]          */
 } moe_layer_weights;
 
-/* Bytes of device workspace moe_layer_fwd needs for `desc` (0 on a bad descriptor). */
+/* Bytes of device workspace moe_layer_fwd needs for `desc` (0 on a bad descriptor;
+ * MOE_MODE_FP8 also needs T * d and moe_rows_bound(T, k, E, m_align) * I <= 2^32 - 256,
+ * the GEMMs' 32-bit operand offsets). */
 size_t moe_layer_workspace_size(const moe_layer_desc *desc);
 
 /* The whole layer forward on one stream, no host synchronisation:
  * route -> dispatch -> (FP8: per-token 1x128 quant) -> grouped GEMM1 with SwiGLU
- * (FP8: requantised 1x128) -> grouped GEMM2 -> combine.
+ * (FP8: requantised 1x128) -> grouped GEMM2 -> combine: y = sum over the top-k experts
+ * of G(x)_i E_i(x) with E_i a SwiGLU FFN (MegaMoE walkthrough, discosf.com, sec.
+ * 2.1-2.2 and 3.2-3.3; hash routing and 4-bit weights, DeepSeek-V4 lecture, tqpw.cn,
+ * sec. 2.2 and 3.1; capacity drop, DeepSeek MoE architecture, mooersco.com, sec. 2.5).
  *   x [T, d]: fp32 (FP32 mode) or bf16; token_ids [T] int64 for hash routing;
  *   y [T, d] output: fp32 (FP32 mode) or bf16;
  *   ws / ws_bytes: caller-owned device workspace (>= moe_layer_workspace_size);

@@ -152,3 +152,29 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_fp8_operands_beyond_32bit_offsets_rejected():
+    """The FP8 GEMMs read activation rows with 32-bit byte offsets: operands whose rows
+    reach past 2^32 - 256 bytes are rejected before any launch."""
+    lib = _lib.load()
+    S = None
+    K = 16384
+    rows = (1 << 32) // K                               # rows * K = 2^32
+    _err(lib.gemm_fp8(FAKE, FAKE, FAKE, FAKE, rows, 128, K, FAKE, S), "32-bit")
+    _err(lib.grouped_gemm_fp8(FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 2, rows, 128, K, 0,
+                              _lib.MOE_BF16, FAKE, None, S), "32-bit")
+    _err(lib.grouped_gemm_fp8_masked(FAKE, FAKE, FAKE, FAKE, FAKE, 4, rows // 4, 128, K, 0,
+                                     _lib.MOE_BF16, FAKE, None, S), "32-bit")
+    D = _lib.MoeLayerDesc
+    # T * d = 600000 * 7168 > 2^32
+    big_t = D(600000, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.0, 16)
+    assert lib.moe_layer_workspace_size(C.byref(big_t)) == 0
+    assert "32-bit" in lib.moe_last_error().decode()
+    # rows * I: T * k * I > 2^32 with T * d below it
+    big_r = D(300000, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.0, 16)
+    assert lib.moe_layer_workspace_size(C.byref(big_r)) == 0
+    assert "32-bit" in lib.moe_last_error().decode()
+    # the same sizes without FP8 operands are accepted (bf16 / fp32 paths use 64-bit)
+    ok = D(300000, 7168, 256, 8, 2048, _lib.MOE_MODE_W4A16, _lib.MOE_ROUTE_SCORE, 0, 0.0, 16)
+    assert lib.moe_layer_workspace_size(C.byref(ok)) > 0

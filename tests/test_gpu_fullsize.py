@@ -5,6 +5,8 @@ tokens of each layer, sampled rows x column blocks of the standalone grouped GEM
 quantising only the expert weights those samples touch.  Integer results that are
 fully checkable (routing of every token, dispatch counts) are checked in full.
 """
+import concurrent.futures as cf
+
 import numpy as np
 import pytest
 import torch
@@ -13,7 +15,8 @@ import fp8_grouped_gemm_amd as M
 import oracle as O
 from oracle import codecs as OC
 import synth
-from gpu_util import (C_MFMA_FP8, TOL, dev, error_ratios, fp8_layer_errors, note, to_np,
+from gpu_util import (C_MFMA_FP8, TOL, check_counts_outside_ties, dev, error_ratios,
+                      fp8_layer_errors, gpu_h_by_slot, note, staged_fp8_layer, to_np,
                       ulp_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -22,16 +25,26 @@ pytestmark = pytest.mark.gpu
 class LazyExperts:
     """Per-expert weights quantised by the oracle on first use, from fp32 masters that
     live on the GPU (generated there by the seeded generator).  Slicing [e:e+1] returns
-    that expert's codes or scales, as layer_forward expects of full arrays."""
+    that expert's codes or scales, as layer_forward expects of full arrays.  prefetch()
+    quantises a set of experts on host threads (numpy releases the GIL in its array
+    loops)."""
 
     def __init__(self, master: torch.Tensor, kind: str):
         self.master, self.kind, self.cache = master, kind, {}
 
+    def _quant(self, w):
+        return OC.quant_fp8_weight(w) if self.kind == "fp8" else OC.int4_quant_rows(w)
+
+    def prefetch(self, experts, threads=16):
+        todo = [int(e) for e in experts if int(e) not in self.cache]
+        hosts = [self.master[e:e + 1].float().cpu().numpy() for e in todo]
+        with cf.ThreadPoolExecutor(threads) as ex:
+            for e, r in zip(todo, ex.map(self._quant, hosts)):
+                self.cache[e] = r
+
     def _get(self, e):
         if e not in self.cache:
-            w = self.master[e:e + 1].float().cpu().numpy()
-            self.cache[e] = (OC.quant_fp8_weight(w) if self.kind == "fp8"
-                             else OC.int4_quant_rows(w))
+            self.cache[e] = self._quant(self.master[e:e + 1].float().cpu().numpy())
         return self.cache[e]
 
     def view(self, which):
@@ -44,8 +57,36 @@ class LazyExperts:
         return _V()
 
 
-def _layer_fullsize(w: synth.Workload, tokens):
-    note(f"full-size layer {w.name} T={w.T} d={w.d} E={w.E} k={w.k} I={w.I} tokens={tokens}")
+def _pick_tokens(idx, counts, near_tie, bms, n_tokens, max_experts):
+    """Tokens for the sampled comparison: greedily the ones adding the fewest experts not
+    yet covered, until ``n_tokens`` are chosen, while making sure both tile classes (groups
+    of at most ``bms`` rows and larger groups) appear.  Near-tie tokens are skipped."""
+    small = set(np.nonzero((counts > 0) & (counts <= bms))[0].tolist())
+    cand = [t for t in range(idx.shape[0]) if not near_tie[t]]
+    chosen, cover = [], set()
+    need_small = 3
+    while len(chosen) < n_tokens and cand:
+        def cost(t):
+            es = set(idx[t].tolist())
+            new = len(es - cover)
+            has_small = len(es & small) > 0
+            return (new - (2 if (need_small > 0 and has_small and es - cover & small) else 0), t)
+        t = min(cand, key=cost)
+        es = set(idx[t].tolist())
+        if len(cover | es) > max_experts:
+            break
+        if es - cover & small:
+            need_small -= 1
+        cover |= es
+        chosen.append(t)
+        cand.remove(t)
+    return chosen, cover, small
+
+
+def _layer_fullsize(w: synth.Workload, tokens=None, n_tokens=16, max_experts=40):
+    """``tokens``: the sampled tokens, or None to choose ``n_tokens`` of them spanning
+    both GEMM tile classes with at most ``max_experts`` distinct experts."""
+    note(f"full-size layer {w.name} T={w.T} d={w.d} E={w.E} k={w.k} I={w.I}")
     d = dev()
     inp = synth.layer_inputs(w, device=d)
     if w.mode == "fp8":
@@ -61,33 +102,60 @@ def _layer_fullsize(w: synth.Workload, tokens):
         weights.update(w_router=inp["w_router"], bias=inp["bias"])
     desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align)
     y, counts = M.moe_layer_fwd(desc, weights, inp["x"], inp.get("token_ids"))
+    staged = None
+    if w.mode == "fp8":
+        note(f"full-size layer {w.name}: the same steps through the individual entry points")
+        staged = staged_fp8_layer(M, w.T, w.E, w.k, w.I, w.m_align, inp["x"], weights)
+        assert torch.equal(staged["y"], y) and torch.equal(staged["counts"], counts)
     torch.cuda.synchronize()
     del q13, q2
-    e13, e2 = LazyExperts(inp["w13"], w.mode), LazyExperts(inp["w2"], w.mode)
-    experts = (e13.view(0), e13.view(1), e2.view(0), e2.view(1))
     ids = inp.get("token_ids")
+    cnt = to_np(counts)
+    near = np.zeros(w.T, bool)
+    if w.route == "score":
+        # routing of every token from the oracle's own fp64 logits (fp32-rounded)
+        xs = inp["x"].float().cpu().numpy()
+        logits = O.router_logits(xs, inp["w_router"].float().cpu().numpy()).astype(np.float32)
+        key = (logits + inp["bias"].cpu().numpy()[None, :]).astype(np.float32).astype(np.float64)
+        srt = -np.sort(-key, axis=1)
+        near = (srt[:, w.k - 1] - srt[:, w.k]) < 1e-4
+        print(f"near-tie tokens {int(near.sum())} of {w.T}")
+    if tokens is None:
+        gidx = to_np(staged["idx"]) if staged is not None else None
+        tokens, cover, small = _pick_tokens(gidx, cnt, near, 16 if w.T * w.k / w.E <= 16
+                                            else 32, n_tokens, max_experts)
+        print(f"sampled tokens {len(tokens)}, experts {len(cover)} "
+              f"({len(cover & small)} in small-row tiles)")
+        live = set(np.nonzero(cnt)[0].tolist())
+        assert len(tokens) >= n_tokens
+        assert (cover & small or not small) and (cover - small or not live - small)
+    tokens = [t for t in tokens if not near[t]]
+    e13, e2 = LazyExperts(inp["w13"], w.mode), LazyExperts(inp["w2"], w.mode)
+    if staged is not None:
+        used = np.unique(to_np(staged["idx"])[tokens])
+        e13.prefetch(used)
+        e2.prefetch(used)
+    experts = (e13.view(0), e13.view(1), e2.view(0), e2.view(1))
     ref = O.layer_forward(w.mode, inp["x"].float().cpu().numpy(), E=w.E, k=w.k, I=w.I,
                           m_align=w.m_align,
                           w_router=None if ids is not None else inp["w_router"].float().cpu().numpy(),
                           bias=None if ids is not None else inp["bias"].cpu().numpy(),
                           token_ids=None if ids is None else ids.cpu().numpy(),
                           experts=experts, tokens=tokens, keep=(w.mode == "fp8"))
-    # routing of every token: identical unless two keys tie within the fp32 logit error
     if w.route == "score":
-        key = ref["logits"].astype(np.float32) + inp["bias"].cpu().numpy()[None, :]
-        srt = -np.sort(-key.astype(np.float64), axis=1)
-        amb = (srt[:, w.k - 1] - srt[:, w.k]) < 1e-4
-        print(f"near-tie tokens {int(amb.sum())} of {w.T}")
-        if not amb.any():
-            np.testing.assert_array_equal(to_np(counts), ref["counts"])
-        tokens = [t for t in tokens if not amb[t]]
+        free = ~near
+        np.testing.assert_array_equal(to_np(staged["idx"])[free], ref["idx"][free])
+        n_checked = check_counts_outside_ties(cnt, ref, inp["bias"].cpu().numpy(), w.k, 1e-4)
+        print(f"routing checked for {int(free.sum())} tokens, counts for {n_checked} experts")
     else:
-        np.testing.assert_array_equal(to_np(counts), ref["counts"])
+        np.testing.assert_array_equal(cnt, ref["counts"])
     yg = to_np(y[tokens]).astype(np.float64)
     if w.mode == "fp8":
-        e = fp8_layer_errors(yg, ref, np.asarray(tokens), w.T, w.k)
+        h_gpu = gpu_h_by_slot(staged, [t * w.k + j for t in tokens for j in range(w.k)])
+        e = fp8_layer_errors(yg, ref, np.asarray(tokens), w.T, w.k, h_gpu)
         print(f"errors {e}")
         assert e["beyond_flip"] <= TOL
+        assert e["beyond_noflip"] <= TOL
     else:
         yr = ref["y"][tokens]
         r = 0.5 * ulp_bf16(yr)
@@ -99,11 +167,12 @@ def _layer_fullsize(w: synth.Workload, tokens):
 
 
 def test_fullsize_prefill_layer():
-    _layer_fullsize(synth.scaled(synth.WORKLOADS["prefill_fp8"], m_align=16), [0, 2049])
+    _layer_fullsize(synth.scaled(synth.WORKLOADS["prefill_fp8"], m_align=16), n_tokens=32,
+                    max_experts=40)
 
 
 def test_fullsize_decode_layer():
-    _layer_fullsize(synth.WORKLOADS["decode_fp8"], [5, 127])
+    _layer_fullsize(synth.WORKLOADS["decode_fp8"], n_tokens=12, max_experts=80)
 
 
 def test_fullsize_hash_w4a16_layer():

@@ -140,6 +140,7 @@ def test_route_from_logits(T, E, k, ties, renorm):
                                               (torch.bfloat16, 70, 7168, 64, 6, True),
                                               (torch.bfloat16, 128, 7168, 256, 8, True),
                                               (torch.bfloat16, 300, 7168, 256, 8, True),
+                                              (torch.bfloat16, 4096, 7168, 256, 8, True),
                                               (torch.bfloat16, 1, 128, 300, 4, True),
                                               (torch.bfloat16, 129, 1024, 520, 8, True),
                                               (torch.bfloat16, 257, 2048, 256, 8, False),
@@ -548,3 +549,9 @@ def test_determinism():
     live[:offsets[-1]] = True
     assert torch.equal(c1[:offsets[-1]], c2[:offsets[-1]])
     assert torch.equal(s1[:offsets[-1]], s2[:offsets[-1]])
+
+
+def test_device_supported():
+    """The GPU these tests run on is a gfx950: the library accepts it."""
+    note("device supported")
+    assert M.moe_device_supported(0)
