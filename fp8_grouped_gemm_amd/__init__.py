@@ -18,7 +18,7 @@ from ._lib import (MOE_BF16, MOE_E4M3, MOE_EPI_PLAIN, MOE_EPI_SWIGLU, MOE_F32, M
                    MOE_ROUTE_RENORM, MOE_ROUTE_SCORE, MoeError, MoeLayerDesc, MoeLayerWeights)
 
 __all__ = [
-    "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route",
+    "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route", "moe_route_noalloc",
     "moe_route_from_logits", "moe_route_hash", "moe_route_workspace_size", "moe_dispatch", "moe_quant_fp8",
     "moe_quant_weight_fp8", "moe_pack_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_fp8_masked",
     "gemm_fp8", "grouped_gemm_w4a16",
@@ -86,6 +86,25 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor, k: in
     _lib.check(_lib_().moe_route(_ptr(x), _dt(x), _ptr(w_router), _ptr(bias), T, d, E, k,
                                  MOE_ROUTE_RENORM if renorm else 0, _ptr(logits), _ptr(idx),
                                  _ptr(w), _ptr(ws), nws, _stream(dev)), "moe_route")
+    return idx, w, logits
+
+
+def moe_route_noalloc(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor, k: int,
+                      renorm: bool = False, out=None):
+    """moe_route with the split-K partials in the library's static device scratch (no
+    device allocation inside the call).  ``out`` = (topk_idx, topk_w, logits) tensors to
+    write, or None to allocate them here with torch.  Returns (topk_idx, topk_w, logits)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T, E), dtype=torch.float32, device=dev))
+    idx, w, logits = out
+    _lib.check(_lib_().moe_route_noalloc(_ptr(x), _dt(x), _ptr(w_router), _ptr(bias), T, d, E,
+                                         k, MOE_ROUTE_RENORM if renorm else 0, _ptr(logits),
+                                         _ptr(idx), _ptr(w), _stream(dev)), "moe_route_noalloc")
     return idx, w, logits
 
 

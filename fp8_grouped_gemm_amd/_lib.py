@@ -47,6 +47,7 @@ SIGNATURES = {
     "moe_rows_bound": (_Z, [_I, _I, _I, _I]),
     "moe_route": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _U, _P, _P, _P, _P, _Z, _P]),
     "moe_route_workspace_size": (_Z, [_I, _I, _I, _I]),
+    "moe_route_noalloc": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _U, _P, _P, _P, _P]),
     "moe_route_from_logits": (_I, [_P, _P, _I, _I, _I, _U, _P, _P, _P]),
     "moe_route_hash": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),

@@ -200,6 +200,37 @@ int moe_route(const void* x, moe_dtype x_dt, const void* w_router, const float* 
                     "topk launch");
 }
 
+int moe_route_noalloc(const void* x, moe_dtype x_dt, const void* w_router, const float* bias,
+                      int T, int d, int E, int k, unsigned flags, float* logits,
+                      int32_t* topk_idx, float* topk_w, void* stream) {
+  REQUIRE(x && w_router, "moe_route_noalloc: null pointer");
+  REQUIRE(x_dt == MOE_BF16 || x_dt == MOE_F32,
+          "moe_route_noalloc: x_dt must be MOE_BF16 or MOE_F32");
+  REQUIRE(d >= 1, "moe_route_noalloc: d must be positive");
+  REQUIRE(x_dt != MOE_BF16 || d % 128 == 0, "moe_route_noalloc: bf16 needs d %% 128 == 0 (got %d)",
+          d);
+  int st = v_route_from_logits(logits, T, E, k, flags, topk_idx, topk_w);
+  if (st) return st;
+  const size_t need = moe_route_workspace_size(T, d, E, x_dt);
+  REQUIRE(need <= moe::kRouteScratchBytes,
+          "moe_route_noalloc: %zu bytes of partial logits exceed the static scratch of %zu bytes "
+          "(T * E too large; use moe_route with a workspace)",
+          need, moe::kRouteScratchBytes);
+  if (T == 0) return MOE_OK;
+  if ((st = current_device(nullptr))) return st;
+  const int n_part = need > 0 ? moe::router_splits(T, d, E, x_dt == MOE_BF16) : 1;
+  void* part = nullptr;
+  if (n_part > 1 && (st = hip_status(moe::route_scratch(&part), "router scratch address")))
+    return st;
+  if ((st = hip_status(moe::launch_router(x, x_dt == MOE_BF16, w_router, logits, T, d, E,
+                                          static_cast<float*>(part), n_part, S(stream)),
+                       "router launch")))
+    return st;
+  return hip_status(moe::launch_topk(logits, static_cast<float*>(part), n_part, bias, T, E, k,
+                                     flags & MOE_ROUTE_RENORM, topk_idx, topk_w, S(stream)),
+                    "topk launch");
+}
+
 int moe_route_hash(const int64_t* token_ids, int T, int E, int32_t* topk_idx, float* topk_w,
                    void* stream) {
   REQUIRE(token_ids && topk_idx && topk_w, "moe_route_hash: null pointer");

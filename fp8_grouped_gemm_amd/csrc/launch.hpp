@@ -14,6 +14,10 @@ hipError_t launch_router(const void* x, bool bf16, const void* w, float* logits,
 // n_part > 1: logits are the plane-order sums of part[n_part][T][E], written by this call
 hipError_t launch_topk(float* logits, const float* part, int n_part, const float* bias, int T,
                        int E, int k, bool renorm, int32_t* idx, float* w, hipStream_t s);
+// Bytes of the router's static device scratch (split-K partial planes of the
+// allocation-free entry point) and its address on the current device.
+constexpr size_t kRouteScratchBytes = size_t(32) << 20;
+hipError_t route_scratch(void** ptr);
 hipError_t launch_hash_route(const int64_t* ids, int T, int E, int32_t* idx, float* w,
                              hipStream_t s);
 hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int m_align, int cap,

@@ -4,6 +4,7 @@
 // The gate is one linear layer followed by softmax(W_g x + b) (MegaMoE walkthrough,
 // discosf.com sec. 2.2) computed in fp32 (DeepSeek-V4 lecture, tqpw.cn sec. 2.3).
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "dma.hpp"
@@ -267,6 +268,35 @@ __global__ void hash_route_kernel(const int64_t* __restrict__ ids, int T, int E,
   uint32_t h = (uint32_t)((uint64_t)ids[t] * 2654435761ull);
   idx[t] = (int32_t)(h % (uint32_t)E);
   w[t] = 1.0f;
+}
+
+// ------------------------------------------------------------- static scratch
+// Device memory of the allocation-free router entry point: the split-K partial planes.
+// One copy per GPU, alive until the process ends; kernels reach it through the address
+// hipGetSymbolAddress returns on that GPU (the array's name is not a device address in
+// host code).  Every call on a GPU shares it, so overlapping calls on one GPU race.
+namespace {
+static __device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t route_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------------ launchers

@@ -104,6 +104,20 @@ int moe_route(const void *x, moe_dtype x_dt, const void *w_router, const float *
 /* Workspace bytes moe_route uses to split the logit product (0: it never splits). */
 size_t moe_route_workspace_size(int T, int d, int E, moe_dtype x_dt);
 
+/* moe_route for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation
+ * and the same outputs, bit for bit, as moe_route given a workspace of
+ * moe_route_workspace_size() bytes, but the split-K partial logits go to a static
+ * device scratch of 32 MiB that the library holds on each GPU it runs on until the
+ * process ends.  The call allocates nothing.  Shapes whose partial logits exceed the
+ * scratch (moe_route_workspace_size(T, d, E, x_dt) > 32 MiB) are rejected with
+ * MOE_ERR_INVALID_ARG before any launch.  Every call on one GPU shares that scratch:
+ * calls that overlap on one GPU (different streams, no ordering between them) race and
+ * must not be issued.  Arguments otherwise as moe_route. */
+int moe_route_noalloc(const void *x, moe_dtype x_dt, const void *w_router, const float *bias,
+                      int T, int d, int E, int k, unsigned flags, float *logits,
+                      int32_t *topk_idx, float *topk_w, void *stream);
+
 /* Top-k of fp32 logits [T, E] with per-expert bias [E] (bias may be NULL = 0): the
  * selection and gate weights of s_i = softmax(W_g x + b_i) (MegaMoE walkthrough,
  * discosf.com, sec. 2.1-2.2; fp32 softmax, DeepSeek-V4 lecture, tqpw.cn, sec. 2.3;
