@@ -224,7 +224,8 @@ def main(argv=None):
                          "clock has left its idle state (it ramps up over tens of ms)")
     ap.add_argument("--workload", default="prefill_fp8",
                     choices=sorted(synth.WORKLOADS) + ["grouped_gemm_fp8", "dense_gemm_fp8",
-                                                       "masked_gemm_fp8"])
+                                                       "masked_gemm_fp8",
+                                                       "decode_fp8_masked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--trace-summary", metavar="DIR",
@@ -255,7 +256,10 @@ def main(argv=None):
     if a.workload == "masked_gemm_fp8":
         print(json.dumps(bench_masked_gemm(M, a.steps, a.warmup, a.settle)), flush=True)
         return 0
-    w = synth.WORKLOADS[a.workload]
+    # the decode layer in the fixed-capacity layout: C = ceil(T k / E) * 2
+    masked = a.workload == "decode_fp8_masked"
+    cap_factor = 2.0 if masked else 0.0
+    w = synth.WORKLOADS["decode_fp8" if masked else a.workload]
     if w.m_align != 16:
         w = synth.scaled(w, m_align=16)     # the kernels' row padding (output unaffected)
     dev = torch.device("cuda:0")
@@ -264,7 +268,9 @@ def main(argv=None):
     inp, weights = make_layer(w, dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
-    desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align)
+    desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align,
+                       capacity_factor=cap_factor, layout="masked" if masked else "contiguous")
+    cap = M.moe_capacity(w.T, w.k, w.E, cap_factor)
     ws = torch.empty(M.moe_layer_workspace_size(desc), dtype=torch.uint8, device=dev)
     x = inp["x"]
     ids = inp.get("token_ids")
@@ -287,13 +293,17 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / a.steps
     cnt = counts.cpu().numpy()
+    if cap > 0:
+        cnt = np.minimum(cnt, cap)          # rows the capacity keeps
     flops, bytes_, g = layer_flops_bytes(w, cnt)
     log(f"layer {ms:.3f} ms/step; rows {g['rows']} touched experts {g['touched']}; "
         f"loads max {cnt.max()} median {int(np.median(cnt))} min {cnt.min()}")
 
     # per-stage times through the individual entry points (same kernels, same stream)
     stages = {}
-    if not a.no_stages and w.mode == "fp8" and w.route == "score":
+    if not a.no_stages and masked:
+        stages = stage_times_masked(M, w, inp, weights, a.steps, cap)
+    elif not a.no_stages and w.mode == "fp8" and w.route == "score":
         stages = stage_times(M, w, inp, weights, a.steps)
     elif not a.no_stages and w.mode == "w4a16" and w.route == "hash":
         stages = stage_times_w4a16(M, w, inp, weights, a.steps)
@@ -341,13 +351,15 @@ def main(argv=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"fp8": "e4m3", "w4a16": "int4xbf16", "fp32": "f32"}[w.mode],
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: T={w.T} d={w.d} E={w.E} top-{w.k} I={w.I}",
+        "config": {"workload": (f"{w.name}{'_masked' if masked else ''}: T={w.T} d={w.d} "
+                                f"E={w.E} top-{w.k} I={w.I}"
+                                + (f", fixed-capacity layout C={cap}" if masked else "")),
                    "mode": w.mode, "route": w.route, "m_align": w.m_align,
                    "skew": f"+{w.skew_add} on {w.skew_frac:.0%} of experts" if w.skew_frac else None},
         "stages_ms": {k: round(v, 4) for k, v in stages.items()} or None,
         "roofline": roofline,
     }
-    if not a.no_cpu_baseline and w.mode == "fp8" and w.route == "score":
+    if not a.no_cpu_baseline and w.mode == "fp8" and w.route == "score" and not masked:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)
@@ -504,18 +516,10 @@ def bench_masked_gemm(M, steps, warmup, settle_s=SETTLE_S):
     inp, weights = make_layer(w, dev)
     idx, _, _ = M.moe_route(inp["x"], inp["w_router"], inp["bias"], w.k)
     cap = M.moe_capacity(w.T, w.k, w.E, 2.0)
-    counts = torch.bincount(idx.flatten().long(), minlength=w.E).to(torch.int32)
-    qx, sx = M.moe_quant_fp8(inp["x"])
-    rows = w.E * cap
-    # each expert's block: its routed tokens first (any order serves the timing)
-    order = torch.argsort(idx.flatten(), stable=True)
-    e_sorted = idx.flatten()[order].long()
-    first = torch.cumsum(counts.long(), 0) - counts.long()
-    pos = torch.arange(order.numel(), device=dev) - first[e_sorted]
-    keep = pos < cap
-    src = torch.zeros(rows, dtype=torch.int64, device=dev)
-    src[(e_sorted * cap + pos)[keep]] = (order // w.k)[keep]
-    qa, sa = qx[src].contiguous(), sx[src].contiguous()
+    # the [E, C, d] layout filled by the library: masked dispatch, then the 1x128
+    # quantiser gathering each row's token (empty rows zero)
+    counts, ros, sor = M.moe_dispatch_masked(idx, w.E, cap)
+    qa, sa = M.moe_quant_fp8(inp["x"], sor, w.k, w.E * cap)
     cnt = torch.clamp(counts, max=cap)
     ms = _time_flushed(lambda: M.grouped_gemm_fp8_masked(qa, sa, weights["w13"], weights["s13"],
                                                           cnt, cap, w.I, swiglu=True),
@@ -563,6 +567,37 @@ def stage_times(M, w, inp, weights, steps):
         torch.cuda.synchronize()
         if it == 0:
             continue        # first pass warms the allocator
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    return {n: acc[n] / steps for n in names}
+
+
+def stage_times_masked(M, w, inp, weights, steps, cap):
+    """Stage times of the fixed-capacity decode layer through the individual C entry
+    points: route -> masked dispatch -> quant-gather into [E, C, d] -> masked GEMM1 ->
+    masked GEMM2 -> combine."""
+    x = inp["x"]
+    names = ["route", "dispatch", "quant", "gemm1", "gemm2", "combine"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = {n: 0.0 for n in names}
+    for it in range(steps + 1):
+        ev[0].record()
+        idx, gw, _ = M.moe_route(x, inp["w_router"], inp["bias"], w.k)
+        ev[1].record()
+        counts, ros, sor = M.moe_dispatch_masked(idx, w.E, cap)
+        ev[2].record()
+        qa, sa = M.moe_quant_fp8(x, sor, w.k, w.E * cap)
+        ev[3].record()
+        hq, sh = M.grouped_gemm_fp8_masked(qa, sa, weights["w13"], weights["s13"], counts, cap,
+                                           w.I, swiglu=True)
+        ev[4].record()
+        o = M.grouped_gemm_fp8_masked(hq, sh, weights["w2"], weights["s2"], counts, cap, w.d)
+        ev[5].record()
+        M.moe_combine(o, ros, gw, w.T, w.k)
+        ev[6].record()
+        torch.cuda.synchronize()
+        if it == 0:
+            continue
         for i, n in enumerate(names):
             acc[n] += ev[i].elapsed_time(ev[i + 1])
     return {n: acc[n] / steps for n in names}

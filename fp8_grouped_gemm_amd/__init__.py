@@ -19,7 +19,8 @@ from ._lib import (MOE_BF16, MOE_E4M3, MOE_EPI_PLAIN, MOE_EPI_SWIGLU, MOE_F32, M
 
 __all__ = [
     "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route", "moe_route_noalloc",
-    "moe_route_from_logits", "moe_route_hash", "moe_route_workspace_size", "moe_dispatch", "moe_quant_fp8",
+    "moe_route_from_logits", "moe_route_hash", "moe_route_workspace_size", "moe_dispatch",
+    "moe_dispatch_masked", "moe_quant_fp8",
     "moe_quant_weight_fp8", "moe_pack_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_fp8_masked",
     "gemm_fp8", "grouped_gemm_w4a16",
     "grouped_gemm_f32", "moe_combine", "moe_layer_workspace_size", "moe_layer_fwd", "MoeError",
@@ -147,6 +148,19 @@ def moe_dispatch(topk_idx: torch.Tensor, E: int, m_align: int, capacity: int = 0
                                     _ptr(offsets), _ptr(ros), _ptr(sor), _stream(dev)),
                "moe_dispatch")
     return counts, offsets, ros, sor
+
+
+def moe_dispatch_masked(topk_idx: torch.Tensor, E: int, capacity: int):
+    """Fixed-capacity layout.  Returns (counts [E], row_of_slot [T*k], slot_of_row [E*C])."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    ros = torch.empty(T * k, dtype=torch.int32, device=dev)
+    sor = torch.empty(E * capacity, dtype=torch.int32, device=dev)
+    _lib.check(_lib_().moe_dispatch_masked(_ptr(topk_idx), T, k, E, capacity, _ptr(counts),
+                                           _ptr(ros), _ptr(sor), _stream(dev)),
+               "moe_dispatch_masked")
+    return counts, ros, sor
 
 
 # --------------------------------------------------------------- quantisation
@@ -292,11 +306,13 @@ class LayerDesc:
     """Python view of moe_layer_desc."""
 
     def __init__(self, T, d, E, k, I, mode="fp8", route="score", renorm=False,
-                 capacity_factor=0.0, m_align=128):
+                 capacity_factor=0.0, m_align=128, layout="contiguous"):
         modes = {"fp32": MOE_MODE_FP32, "fp8": MOE_MODE_FP8, "w4a16": MOE_MODE_W4A16}
+        layouts = {"contiguous": _lib.MOE_LAYOUT_CONTIGUOUS, "masked": _lib.MOE_LAYOUT_MASKED}
         self.c = MoeLayerDesc(T, d, E, k, I, modes[mode],
                               MOE_ROUTE_HASH if route == "hash" else MOE_ROUTE_SCORE,
-                              MOE_ROUTE_RENORM if renorm else 0, float(capacity_factor), m_align)
+                              MOE_ROUTE_RENORM if renorm else 0, float(capacity_factor), m_align,
+                              layouts[layout])
 
 
 def moe_layer_workspace_size(desc: LayerDesc) -> int:

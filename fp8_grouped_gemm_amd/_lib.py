@@ -21,6 +21,7 @@ MOE_ROUTE_RENORM = 1
 MOE_EPI_PLAIN, MOE_EPI_SWIGLU = 0, 1
 MOE_MODE_FP32, MOE_MODE_FP8, MOE_MODE_W4A16 = 0, 1, 2
 MOE_ROUTE_SCORE, MOE_ROUTE_HASH = 0, 1
+MOE_LAYOUT_CONTIGUOUS, MOE_LAYOUT_MASKED = 0, 1
 
 _P = C.c_void_p
 _I = C.c_int
@@ -31,7 +32,8 @@ _Z = C.c_size_t
 
 class MoeLayerDesc(C.Structure):
     _fields_ = [("T", _I), ("d", _I), ("E", _I), ("k", _I), ("I", _I), ("mode", _I),
-                ("route", _I), ("route_flags", _U), ("capacity_factor", _D), ("m_align", _I)]
+                ("route", _I), ("route_flags", _U), ("capacity_factor", _D), ("m_align", _I),
+                ("layout", _I)]
 
 
 class MoeLayerWeights(C.Structure):
@@ -51,6 +53,7 @@ SIGNATURES = {
     "moe_route_from_logits": (_I, [_P, _P, _I, _I, _I, _U, _P, _P, _P]),
     "moe_route_hash": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_dispatch_masked": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_quant_fp8": (_I, [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P]),
     "moe_quant_weight_fp8": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_pack_weight_fp8": (_I, [_P, _I, _I, _I, _P, _P]),

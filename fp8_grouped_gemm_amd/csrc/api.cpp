@@ -255,6 +255,23 @@ int moe_dispatch(const int32_t* topk_idx, int T, int k, int E, int m_align, int 
                     "dispatch launch");
 }
 
+int moe_dispatch_masked(const int32_t* topk_idx, int T, int k, int E, int capacity,
+                        int32_t* counts, int32_t* row_of_slot, int32_t* slot_of_row,
+                        void* stream) {
+  REQUIRE(counts && slot_of_row, "moe_dispatch_masked: null pointer");
+  REQUIRE((topk_idx && row_of_slot) || T == 0, "moe_dispatch_masked: null pointer");
+  REQUIRE(T >= 0 && k >= 1 && E >= 1 && E <= 65536, "moe_dispatch_masked: bad T/k/E (%d/%d/%d)",
+          T, k, E);
+  REQUIRE(capacity >= 1, "moe_dispatch_masked: capacity must be >= 1 (got %d)", capacity);
+  REQUIRE((long long)E * capacity < (1LL << 31) && (long long)T * k < (1LL << 31),
+          "moe_dispatch_masked: E * capacity overflows int32");
+  int st = current_device(nullptr);
+  if (st) return st;
+  return hip_status(moe::launch_dispatch(topk_idx, T, k, E, 1, capacity, counts, nullptr,
+                                         row_of_slot, slot_of_row, E * capacity, S(stream), true),
+                    "masked dispatch launch");
+}
+
 int moe_quant_fp8(const void* x, moe_dtype x_dt, int rows_in, int K, const int32_t* src_row,
                   int src_div, int rows_out, uint8_t* q, float* scales, void* stream) {
   REQUIRE(x && q && scales, "moe_quant_fp8: null pointer");
@@ -456,6 +473,8 @@ int layer_check(const moe_layer_desc* d) {
           d->route);
   REQUIRE(d->route != MOE_ROUTE_HASH || d->k == 1, "moe_layer: hash routing needs k = 1");
   REQUIRE((d->route_flags & ~MOE_ROUTE_RENORM) == 0, "moe_layer: unknown route flags");
+  REQUIRE(d->layout == MOE_LAYOUT_CONTIGUOUS || d->layout == MOE_LAYOUT_MASKED,
+          "moe_layer: unknown layout %d", d->layout);
   REQUIRE(std::isfinite(d->capacity_factor), "moe_layer: capacity_factor must be finite");
   REQUIRE(d->m_align >= 1 && d->m_align <= 1024, "moe_layer: m_align must be in [1, 1024]");
   REQUIRE(d->d % 128 == 0, "moe_layer: d must be a multiple of 128");
@@ -475,13 +494,29 @@ int layer_check(const moe_layer_desc* d) {
   if (d->mode == MOE_MODE_FP32) REQUIRE(d->I % 16 == 0, "moe_layer: fp32 needs I %% 16 == 0");
   REQUIRE((long long)d->T * d->k + (long long)d->E * (d->m_align - 1) < (1LL << 31),
           "moe_layer: rows bound overflows int32");
+  if (d->layout == MOE_LAYOUT_MASKED) {
+    REQUIRE(d->mode == MOE_MODE_FP8, "moe_layer: the masked layout needs MOE_MODE_FP8");
+    const int cap = moe_capacity(d->T, d->k, d->E, d->capacity_factor);
+    REQUIRE(cap >= 1, "moe_layer: the masked layout needs capacity_factor > 0 "
+                      "(capacity floor(ceil(T*k/E) * factor) >= 1)");
+    REQUIRE((long long)d->E * cap * std::max(d->d, d->I) <= kMaxOperandBytes,
+            "moe_layer: E * capacity rows exceed the 32-bit operand offset range");
+  }
   return MOE_OK;
+}
+
+// rows of the expert-row buffers: E * capacity (masked) or the contiguous bound
+long long layer_rows(const moe_layer_desc* d) {
+  if (d->layout == MOE_LAYOUT_MASKED)
+    return (long long)d->E * moe_capacity(d->T, d->k, d->E, d->capacity_factor);
+  return (long long)moe_rows_bound(d->T, d->k, d->E, d->m_align);
 }
 
 LayerWs layer_ws(const moe_layer_desc* d) {
   LayerWs L{};
   const size_t T = d->T, E = d->E, k = d->k, D = d->d, I = d->I;
-  const size_t R = moe_rows_bound(d->T, d->k, d->E, d->m_align);
+  const size_t R = (size_t)layer_rows(d);
+  const bool masked = d->layout == MOE_LAYOUT_MASKED;
   size_t p = 0;
   auto take = [&](size_t bytes) { size_t at = p; p = align_up(p + bytes); return at; };
   L.part = take(d->route == MOE_ROUTE_SCORE && d->mode != MOE_MODE_FP32
@@ -494,8 +529,9 @@ LayerWs layer_ws(const moe_layer_desc* d) {
   L.ros = take(T * k * 4);
   L.sor = take(R * 4);
   if (d->mode == MOE_MODE_FP8) {
-    L.qx = take(T * D);
-    L.sx = take(T * (D / 128) * 4);
+    // masked: the expert-row buffer [E, C, d] of gathered token codes
+    L.qx = take((masked ? R : T) * D);
+    L.sx = take((masked ? R : T) * (D / 128) * 4);
     L.h = take(R * I);
     L.sh = take(R * (I / 128) * 4);
     L.o = take(R * D * 2);
@@ -546,8 +582,9 @@ int moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* w, const voi
   int32_t* ros = reinterpret_cast<int32_t*>(base + L.ros);
   int32_t* sor = reinterpret_cast<int32_t*>(base + L.sor);
   const int T = d->T, D = d->d, E = d->E, k = d->k, I = d->I;
-  const int R = (int)moe_rows_bound(T, k, E, d->m_align);
+  const int R = (int)layer_rows(d);
   const bool f32 = d->mode == MOE_MODE_FP32;
+  const bool masked = d->layout == MOE_LAYOUT_MASKED;
 
 #define STEP(expr, what) \
   if ((st = hip_status((expr), what))) return st;
@@ -565,11 +602,28 @@ int moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* w, const voi
   }
   const int cap = moe_capacity(T, k, E, d->capacity_factor);
   if (cap < 0) return cap;
-  STEP(moe::launch_dispatch(idx, T, k, E, d->m_align, cap, counts, offsets, ros, sor, R, s),
+  STEP(moe::launch_dispatch(idx, T, k, E, d->m_align, cap, counts, masked ? nullptr : offsets,
+                            ros, sor, R, s, masked),
        "dispatch launch");
   const double rows_per_group = (double)R / E;
   void* o = base + L.o;
-  if (d->mode == MOE_MODE_FP8) {
+  if (d->mode == MOE_MODE_FP8 && masked) {
+    // fixed-capacity layout: token codes gathered into [E, C, d] (empty rows zero), then
+    // both GEMMs over per-expert row counts clamped to C
+    uint8_t* qa = base + L.qx;
+    float* sa = reinterpret_cast<float*>(base + L.sx);
+    uint8_t* hq = base + L.h;
+    float* sh = reinterpret_cast<float*>(base + L.sh);
+    STEP(moe::launch_quant_act(x, true, D, sor, k, R, qa, sa, s), "quant-gather launch");
+    STEP(moe::launch_gemm_fp8(qa, sa, nullptr, 1, static_cast<const uint8_t*>(w->w13), w->s13,
+                              counts, E, R, I, D, true, hq, sh, pick_bm(cap), cus, s,
+                              moe::kRowsMasked, cap),
+         "masked gemm1 launch");
+    STEP(moe::launch_gemm_fp8(hq, sh, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
+                              counts, E, R, D, I, false, o, nullptr, pick_bm(cap), cus, s,
+                              moe::kRowsMasked, cap),
+         "masked gemm2 launch");
+  } else if (d->mode == MOE_MODE_FP8) {
     uint8_t* qx = base + L.qx;
     float* sx = reinterpret_cast<float*>(base + L.sx);
     uint8_t* hq = base + L.h;

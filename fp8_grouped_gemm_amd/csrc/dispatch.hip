@@ -4,7 +4,9 @@
 // (expert grouping, MegaMoE walkthrough, discosf.com sec. 2.1), each block padded
 // to a multiple of m_align so the grouped GEMM's row tiles stay inside one expert.
 // An optional capacity keeps the first C slots of each expert and drops the rest
-// silently (DeepSeek MoE architecture, mooersco.com sec. 2.5).
+// silently (DeepSeek MoE architecture, mooersco.com sec. 2.5).  In the fixed-capacity
+// ("masked") layout every expert owns exactly C rows, expert e rows [e C, e C + C)
+// whatever its count (the second grouped layout of DeepGEMM, qidao123.com day 3).
 //
 // Ranks come from integer counts and lane masks only, so the result does not depend on
 // scheduling.  Up to 512 experts one workgroup does it all (dispatch_fused_kernel);
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
-    const int32_t* __restrict__ idx, int n_slots, int E, int m_align, int cap,
+    const int32_t* __restrict__ idx, int n_slots, int E, int m_align, int cap, bool fixed,
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_of_slot, int32_t* __restrict__ slot_of_row, int rows_bound) {
   __shared__ int red[4];
@@ -50,19 +52,19 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   int before = 0, all = 0;
   for (int j = tid; j < E; j += 256) {
     int kept = cap > 0 ? min(counts[j], cap) : counts[j];
-    int padded = (kept + m_align - 1) / m_align * m_align;
+    int padded = fixed ? cap : (kept + m_align - 1) / m_align * m_align;
     all += padded;
     if (j < e) before += padded;
   }
   before = block_sum_256(before, red);
   all = block_sum_256(all, red);
-  if (tid == 0) {
+  if (tid == 0 && offsets) {
     offsets[e] = before;
     if (e == E - 1) offsets[E] = all;
   }
   const int cnt = counts[e];
   const int kept = cap > 0 ? min(cnt, cap) : cnt;
-  const int padded = (kept + m_align - 1) / m_align * m_align;
+  const int padded = fixed ? cap : (kept + m_align - 1) / m_align * m_align;
 
   // stable scatter: rank of each matching slot = matches before it in slot order
   int running = 0;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 // advances the expert's row.  Slot order inside every expert is thus preserved.
 template <int EMAX>
 __global__ __launch_bounds__(1024) void dispatch_fused_kernel(
-    const int32_t* __restrict__ idx, int n_slots, int E, int m_align, int cap,
+    const int32_t* __restrict__ idx, int n_slots, int E, int m_align, int cap, bool fixed,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_of_slot, int32_t* __restrict__ slot_of_row, int rows_bound) {
   constexpr int NW = 16;
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(
 #pragma unroll
     for (int v = 0; v < NW; ++v) total += cnt[v][tid];
     const int kept = cap > 0 ? min(total, cap) : total;
-    padded = (kept + m_align - 1) / m_align * m_align;
+    padded = fixed ? cap : (kept + m_align - 1) / m_align * m_align;
     kept_s[tid] = kept;
     counts[tid] = total;
   }
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(
   const int excl = before + incl - padded;
   if (tid < E) {
     off_s[tid] = excl;
-    offsets[tid] = excl;
+    if (offsets) offsets[tid] = excl;
     int run = excl;                                // first row of each segment's slots
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(
   }
   if (tid == E - 1) {
     off_s[E] = excl + padded;
-    offsets[E] = excl + padded;
+    if (offsets) offsets[E] = excl + padded;
   }
   __syncthreads();
 
@@ -192,23 +194,23 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(
 
 hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int m_align, int cap,
                            int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
-                           int32_t* slot_of_row, int rows_bound, hipStream_t s) {
+                           int32_t* slot_of_row, int rows_bound, hipStream_t s, bool fixed) {
   const int n = T * k;
   if (E <= 256) {
     hipLaunchKernelGGL(dispatch_fused_kernel<256>, dim3(1), dim3(1024), 0, s, idx, n, E, m_align,
-                       cap, counts, offsets, row_of_slot, slot_of_row, rows_bound);
+                       cap, fixed, counts, offsets, row_of_slot, slot_of_row, rows_bound);
     return hipGetLastError();
   }
   if (E <= 512) {
     hipLaunchKernelGGL(dispatch_fused_kernel<512>, dim3(1), dim3(1024), 0, s, idx, n, E, m_align,
-                       cap, counts, offsets, row_of_slot, slot_of_row, rows_bound);
+                       cap, fixed, counts, offsets, row_of_slot, slot_of_row, rows_bound);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(E), dim3(256), 0, s, idx, n, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(E), dim3(256), 0, s, idx, n, E, m_align, cap,
-                     counts, offsets, row_of_slot, slot_of_row, rows_bound);
+                     fixed, counts, offsets, row_of_slot, slot_of_row, rows_bound);
   return hipGetLastError();
 }
 

@@ -20,9 +20,11 @@ constexpr size_t kRouteScratchBytes = size_t(32) << 20;
 hipError_t route_scratch(void** ptr);
 hipError_t launch_hash_route(const int64_t* ids, int T, int E, int32_t* idx, float* w,
                              hipStream_t s);
+// fixed: the masked layout, every expert owning exactly cap rows (offsets may be null)
 hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int m_align, int cap,
                            int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
-                           int32_t* slot_of_row, int rows_bound, hipStream_t s);
+                           int32_t* slot_of_row, int rows_bound, hipStream_t s,
+                           bool fixed = false);
 hipError_t launch_quant_act(const void* x, bool bf16, int K, const int32_t* src_row, int src_div,
                             int rows_out, uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_quant_weight_fp8(const float* w, int G, int N, int K, uint8_t* q,

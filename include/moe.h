@@ -67,6 +67,8 @@ typedef enum {
 #define MOE_MODE_FP32 0   /* fp32 activations and weights, no quantisation            */
 #define MOE_MODE_FP8 1    /* e4m3 weights with 128x128 scales, 1x128 activation quant */
 #define MOE_MODE_W4A16 2  /* int4 weights with 1x128 per-channel scales, bf16 acts    */
+#define MOE_LAYOUT_CONTIGUOUS 0 /* expert rows concatenated, each padded to m_align   */
+#define MOE_LAYOUT_MASKED 1     /* fixed capacity: expert e owns rows [e C, e C + C)    */
 #define MOE_ROUTE_SCORE 0 /* biased softmax top-k over router logits                  */
 #define MOE_ROUTE_HASH 1  /* expert = ((id * 2654435761) mod 2^32) mod E, weight 1, k=1 */
 
@@ -149,6 +151,22 @@ int moe_route_hash(const int64_t *token_ids, int T, int E, int32_t *topk_idx,
 int moe_dispatch(const int32_t *topk_idx, int T, int k, int E, int m_align, int capacity,
                  int32_t *counts, int32_t *offsets, int32_t *row_of_slot,
                  int32_t *slot_of_row, void *stream);
+
+/* Dispatch into the fixed-capacity ("masked") expert layout, the second grouped layout
+ * DeepGEMM offers beside the contiguous one (qidao123.com day 3), with the capacity of
+ * DeepSeek MoE architecture, mooersco.com sec. 2.5: expert e owns rows [e*C, e*C + C)
+ * whatever its count; its first min(counts[e], C) slots in slot order take rows e*C,
+ * e*C + 1, ... and the rest are dropped silently.  C = capacity (>= 1, e.g. from
+ * moe_capacity).  Slot s = t*k + j.
+ *   counts [E]          slots routed to each expert (before capacity; the masked GEMM
+ *                       clamps them to C)
+ *   row_of_slot [T*k]   row of each slot, -1 if dropped
+ *   slot_of_row [E*C]   inverse map, -1 on rows no slot took
+ * topk_idx [T, k] int32 in [0, E) (with E <= 512 a slot outside that range is dropped).
+ * Integer-only and deterministic; the same ranks as moe_dispatch with this capacity. */
+int moe_dispatch_masked(const int32_t *topk_idx, int T, int k, int E, int capacity,
+                        int32_t *counts, int32_t *row_of_slot, int32_t *slot_of_row,
+                        void *stream);
 
 /* 1x128 e4m3 activation quantisation (discosf.com sec. 3.3; fine-grained scales,
  * qidao123.com day 3).  For output row r, source row i = src_row ? src_row[r] / src_div
@@ -259,6 +277,9 @@ typedef struct {
   unsigned route_flags;    /* MOE_ROUTE_RENORM                                      */
   double capacity_factor;  /* <= 0: dropless                                        */
   int m_align;             /* row padding quantum of each expert (1..1024)          */
+  int layout;              /* MOE_LAYOUT_CONTIGUOUS, or MOE_LAYOUT_MASKED (FP8 mode  */
+                           /* with capacity_factor > 0: buffers [E, C, *], C =      */
+                           /* moe_capacity(T, k, E, capacity_factor))               */
 } moe_layer_desc;
 
 typedef struct {
@@ -287,8 +308,10 @@ size_t moe_layer_workspace_size(const moe_layer_desc *desc);
  *   y [T, d] output: fp32 (FP32 mode) or bf16;
  *   ws / ws_bytes: caller-owned device workspace (>= moe_layer_workspace_size);
  *   counts_out [E] int32 (may be NULL): routed slots per expert.
- * GEMM1 reads activation rows through the dispatch map, so no gathered copy of the
- * activations is made. */
+ * Contiguous layout: GEMM1 reads activation rows through the dispatch map, so no
+ * gathered copy of the activations is made.  Masked layout: moe_dispatch_masked, the
+ * token codes gathered into the [E, C, d] buffer (1x128 quantisation, empty rows zero),
+ * the masked GEMM1 and GEMM2 over counts clamped to C, then the combine. */
 int moe_layer_fwd(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
                   const int64_t *token_ids, void *y, void *ws, size_t ws_bytes,
                   int32_t *counts_out, void *stream);

@@ -131,6 +131,35 @@ def dispatch(idx, E: int, m_align: int, cap: int = 0):
     return counts, offsets, row_of_slot, slot_of_row
 
 
+def dispatch_masked(idx, E: int, cap: int):
+    """The fixed-capacity ("masked") expert layout, the second grouped layout of DeepGEMM's
+    release notes (qidao123.com day 3), with the capacity rule of mooersco.com sec. 2.5:
+    expert e owns the C = ``cap`` rows [e*C, e*C + C) whatever its load; its slots, in
+    (token, slot) order, take rows e*C, e*C + 1, ... until the C rows are full, and the
+    slots past them are dropped silently.
+    Returns counts [E] (slots routed, before capacity), row_of_slot [T*k] (-1 = dropped)
+    and slot_of_row [E*C] (-1 = row left empty).
+    """
+    if cap < 1:
+        raise ValueError("dispatch_masked: capacity must be >= 1")
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    flat = idx.ravel()
+    if flat.size and (flat.min() < 0 or flat.max() >= E):
+        raise ValueError("dispatch_masked: expert id out of range")
+    counts = np.zeros(E, dtype=np.int32)
+    row_of_slot = np.full(T * k, -1, dtype=np.int32)
+    slot_of_row = np.full(E * cap, -1, dtype=np.int32)
+    for s in range(T * k):                 # slots in (token, slot) order
+        e = flat[s]
+        r = counts[e]
+        counts[e] += 1
+        if r < cap:
+            row_of_slot[s] = e * cap + r
+            slot_of_row[e * cap + r] = s
+    return counts, row_of_slot, slot_of_row
+
+
 # ----------------------------------------------------------------- expert math
 
 def grouped_gemm(A, B, offsets) -> np.ndarray:

@@ -23,7 +23,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = _lib.load()
     declared = _declared()
-    assert len(declared) == 22, declared
+    assert len(declared) == 23, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -178,3 +178,29 @@ def test_fp8_operands_beyond_32bit_offsets_rejected():
     # the same sizes without FP8 operands are accepted (bf16 / fp32 paths use 64-bit)
     ok = D(300000, 7168, 256, 8, 2048, _lib.MOE_MODE_W4A16, _lib.MOE_ROUTE_SCORE, 0, 0.0, 16)
     assert lib.moe_layer_workspace_size(C.byref(ok)) > 0
+
+
+def test_masked_dispatch_and_layout_checks():
+    lib = _lib.load()
+    S = None
+    _err(lib.moe_dispatch_masked(FAKE, 4, 2, 8, 0, FAKE, FAKE, FAKE, S), "capacity")
+    _err(lib.moe_dispatch_masked(FAKE, 4, 2, 8, 4, None, FAKE, FAKE, S), "null")
+    D = _lib.MoeLayerDesc
+    # decode shape, capacity ceil(128*8/256) * 2 = 8: buffers of 256 * 8 rows
+    m = D(128, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 2.0, 16,
+          _lib.MOE_LAYOUT_MASKED)
+    n = lib.moe_layer_workspace_size(C.byref(m))
+    rows = 256 * 8
+    assert n >= rows * 7168 + rows * 2048 + rows * 7168 * 2
+    assert n < (rows * 7168 + rows * 2048 + rows * 7168 * 2) * 1.1
+    no_cap = D(128, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.0, 16,
+               _lib.MOE_LAYOUT_MASKED)
+    assert lib.moe_layer_workspace_size(C.byref(no_cap)) == 0
+    assert "capacity_factor" in lib.moe_last_error().decode()
+    w4 = D(128, 7168, 256, 8, 2048, _lib.MOE_MODE_W4A16, _lib.MOE_ROUTE_SCORE, 0, 2.0, 16,
+           _lib.MOE_LAYOUT_MASKED)
+    assert lib.moe_layer_workspace_size(C.byref(w4)) == 0
+    assert "MOE_MODE_FP8" in lib.moe_last_error().decode()
+    bad = D(128, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 2.0, 16, 7)
+    assert lib.moe_layer_workspace_size(C.byref(bad)) == 0
+    assert "layout" in lib.moe_last_error().decode()

@@ -83,10 +83,12 @@ def _pick_tokens(idx, counts, near_tie, bms, n_tokens, max_experts):
     return chosen, cover, small
 
 
-def _layer_fullsize(w: synth.Workload, tokens=None, n_tokens=16, max_experts=40):
+def _layer_fullsize(w: synth.Workload, tokens=None, n_tokens=16, max_experts=40,
+                    cap_factor=0.0, layout="contiguous"):
     """``tokens``: the sampled tokens, or None to choose ``n_tokens`` of them spanning
     both GEMM tile classes with at most ``max_experts`` distinct experts."""
-    note(f"full-size layer {w.name} T={w.T} d={w.d} E={w.E} k={w.k} I={w.I}")
+    note(f"full-size layer {w.name} T={w.T} d={w.d} E={w.E} k={w.k} I={w.I} "
+         f"cap_factor={cap_factor} layout={layout}")
     d = dev()
     inp = synth.layer_inputs(w, device=d)
     if w.mode == "fp8":
@@ -100,12 +102,14 @@ def _layer_fullsize(w: synth.Workload, tokens=None, n_tokens=16, max_experts=40)
     weights = {"w13": q13, "s13": s13, "w2": q2, "s2": s2}
     if w.route == "score":
         weights.update(w_router=inp["w_router"], bias=inp["bias"])
-    desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align)
+    desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align,
+                       capacity_factor=cap_factor, layout=layout)
     y, counts = M.moe_layer_fwd(desc, weights, inp["x"], inp.get("token_ids"))
     staged = None
     if w.mode == "fp8":
         note(f"full-size layer {w.name}: the same steps through the individual entry points")
-        staged = staged_fp8_layer(M, w.T, w.E, w.k, w.I, w.m_align, inp["x"], weights)
+        staged = staged_fp8_layer(M, w.T, w.E, w.k, w.I, w.m_align, inp["x"], weights,
+                                  capacity=M.moe_capacity(w.T, w.k, w.E, cap_factor))
         assert torch.equal(staged["y"], y) and torch.equal(staged["counts"], counts)
     torch.cuda.synchronize()
     del q13, q2
@@ -141,7 +145,8 @@ def _layer_fullsize(w: synth.Workload, tokens=None, n_tokens=16, max_experts=40)
                           w_router=None if ids is not None else inp["w_router"].float().cpu().numpy(),
                           bias=None if ids is not None else inp["bias"].cpu().numpy(),
                           token_ids=None if ids is None else ids.cpu().numpy(),
-                          experts=experts, tokens=tokens, keep=(w.mode == "fp8"))
+                          experts=experts, tokens=tokens, keep=(w.mode == "fp8"),
+                          cap_factor=cap_factor)
     if w.route == "score":
         free = ~near
         np.testing.assert_array_equal(to_np(staged["idx"])[free], ref["idx"][free])
@@ -173,6 +178,12 @@ def test_fullsize_prefill_layer():
 
 def test_fullsize_decode_layer():
     _layer_fullsize(synth.WORKLOADS["decode_fp8"], n_tokens=12, max_experts=80)
+
+
+def test_fullsize_decode_layer_masked():
+    """The decode layer in the fixed-capacity layout, C = ceil(128*8/256) * 2 = 8."""
+    _layer_fullsize(synth.WORKLOADS["decode_fp8"], n_tokens=12, max_experts=80,
+                    cap_factor=2.0, layout="masked")
 
 
 def test_fullsize_hash_w4a16_layer():

@@ -203,6 +203,20 @@ def test_dispatch_bitexact(T, E, k, m_align, cap):
     np.testing.assert_array_equal(to_np(sor), so)
 
 
+@pytest.mark.parametrize("T,E,k,cap", [(128, 256, 8, 8), (333, 13, 3, 40), (333, 13, 3, 200),
+                                       (200, 700, 2, 3), (1, 4, 2, 1), (4096, 256, 8, 160)])
+def test_dispatch_masked_bitexact(T, E, k, cap):
+    """Fixed-capacity layout: counts, row_of_slot and slot_of_row [E*C] bit-exact, with and
+    without drops, on the one-workgroup kernel and the per-expert kernels (E > 512)."""
+    note(f"dispatch masked T={T} E={E} k={k} cap={cap}")
+    idx = synth.random_topk(T, E, k, seed=T + E + 1, skew=1.1)
+    counts, ros, sor = M.moe_dispatch_masked(torch.from_numpy(idx).to(dev()), E, cap)
+    co, ro, so = O.dispatch_masked(idx, E, cap)
+    np.testing.assert_array_equal(to_np(counts), co)
+    np.testing.assert_array_equal(to_np(ros), ro)
+    np.testing.assert_array_equal(to_np(sor), so)
+
+
 # ---------------------------------------------------------------- grouped GEMM
 
 def _gemm_case(sizes, N, K, m_align, seed, swiglu):

@@ -49,13 +49,14 @@ def _near_ties(logits32, bias, k, margin):
     return (srt[:, k - 1] - srt[:, k]) < margin
 
 
-def run_layer_case(w: synth.Workload, tokens=None, cap_factor=0.0, renorm=False):
+def run_layer_case(w: synth.Workload, tokens=None, cap_factor=0.0, renorm=False,
+                   layout="contiguous"):
     note(f"layer {w.name} T={w.T} d={w.d} E={w.E} k={w.k} I={w.I} mode={w.mode} "
-         f"cap_factor={cap_factor} renorm={renorm}")
+         f"cap_factor={cap_factor} renorm={renorm} layout={layout}")
     inp = synth.layer_inputs(w)
     gw = _gpu_weights(w, inp)
     desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align,
-                       capacity_factor=cap_factor, renorm=renorm)
+                       capacity_factor=cap_factor, renorm=renorm, layout=layout)
     x = inp["x"].to(dev())
     ids = inp.get("token_ids")
     y, counts = M.moe_layer_fwd(desc, gw, x, ids.to(dev()) if ids is not None else None)
@@ -65,6 +66,7 @@ def run_layer_case(w: synth.Workload, tokens=None, cap_factor=0.0, renorm=False)
         # expose GEMM1's requantised h for the flip accounting below
         staged = staged_fp8_layer(M, w.T, w.E, w.k, w.I, w.m_align, x, gw, renorm=renorm,
                                   capacity=M.moe_capacity(w.T, w.k, w.E, cap_factor))
+        # (masked layout: the same expert rows at other places, so the same y bit for bit)
         assert torch.equal(staged["y"], y) and torch.equal(staged["counts"], counts)
     torch.cuda.synchronize()
     ref = O.layer_forward(w.mode, inp["x"].float().numpy(), E=w.E, k=w.k, I=w.I,
@@ -148,6 +150,15 @@ def test_layer_capacity_drop(mode):
     dropped = int(np.maximum(np.asarray(ref["counts"]) - cap, 0).sum())
     print(f"capacity {cap}, dropped slots {dropped}")
     assert dropped > 0
+
+
+@pytest.mark.parametrize("cap_factor", [1.0, 2.0])
+def test_layer_masked_layout(cap_factor):
+    """Fixed-capacity layout ([E, C, d] buffers, masked GEMMs): the oracle's layer with that
+    capacity, and bit for bit the contiguous layout with the same capacity."""
+    w = synth.Workload("masked_fp8", T=96, d=256, E=8, k=2, I=256, mode="fp8",
+                       skew_frac=0.25, skew_add=2.0, m_align=16, seed=5)
+    run_layer_case(w, cap_factor=cap_factor, layout="masked")
 
 
 def test_layer_small_w4a16_hash():

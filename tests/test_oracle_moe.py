@@ -130,6 +130,39 @@ def test_dispatch_invariants(cap, m_align):
     assert len(sor) == T * k + E * (m_align - 1)
 
 
+@pytest.mark.parametrize("cap", [1, 4, 40])
+def test_dispatch_masked_layout(cap):
+    """Fixed-capacity layout: expert e's rows are [e C, e C + C) whatever its load, filled
+    by its first C slots in slot order (numpy's stable argsort decides the order here, a
+    different route from the oracle's slot loop); the same ranks and drops as the
+    contiguous dispatch with that capacity."""
+    T, k, E = 61, 3, 9
+    idx = synth.random_topk(T, E, k, seed=7, skew=1.3)
+    counts, ros, sor = O.dispatch_masked(idx, E, cap)
+    flat = idx.ravel()
+    assert [int(np.sum(flat == e)) for e in range(E)] == list(counts)
+    order = np.argsort(flat, kind="stable")
+    want_ros = np.full(T * k, -1, np.int64)
+    start = np.concatenate([[0], np.cumsum(counts)])
+    for e in range(E):
+        for r, s_ in enumerate(order[start[e]:start[e + 1]]):
+            if r < cap:
+                want_ros[s_] = e * cap + r
+    np.testing.assert_array_equal(ros, want_ros)
+    assert len(sor) == E * cap
+    for row in range(E * cap):
+        s_ = sor[row]
+        assert (s_ == -1) if row % cap >= min(counts[row // cap], cap) else ros[s_] == row
+    # relation to the contiguous layout with the same capacity: same kept slots, each
+    # expert's block moved from offsets[e] to e * C
+    c2, offsets, ros2, _ = O.dispatch(idx, E, 1, cap)
+    np.testing.assert_array_equal(counts, c2)
+    kept = ros2 >= 0
+    np.testing.assert_array_equal(ros >= 0, kept)
+    e_of = flat[kept]
+    np.testing.assert_array_equal(ros[kept] - e_of * cap, ros2[kept] - offsets[e_of])
+
+
 # ------------------------------------------------------------- grouped GEMM
 
 def _frac(x):
