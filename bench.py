@@ -226,6 +226,9 @@ def main(argv=None):
                     choices=sorted(synth.WORKLOADS) + ["grouped_gemm_fp8", "dense_gemm_fp8",
                                                        "masked_gemm_fp8",
                                                        "decode_fp8_masked"])
+    ap.add_argument("--chunk-tokens", type=int, default=0,
+                    help="time the two-stream chunk pipeline (moe_layer_fwd_chunked) with "
+                         "chunks of this many tokens instead of the single pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--trace-summary", metavar="DIR",
@@ -280,6 +283,16 @@ def main(argv=None):
     def step():
         M.moe_layer_fwd(desc, weights, x, ids, workspace=ws, y=y, counts=counts)
 
+    if a.chunk_tokens:
+        step()                              # counts of the whole batch, for the accounting
+        ws_c = torch.empty(M.moe_layer_chunked_workspace_size(desc, a.chunk_tokens),
+                           dtype=torch.uint8, device=dev)
+        aux = torch.cuda.Stream(device=dev)
+
+        def step():                         # noqa: F811
+            M.moe_layer_fwd_chunked(desc, weights, x, a.chunk_tokens, token_ids=ids,
+                                    workspace=ws_c, y=y, aux_stream=aux)
+
     settle(step, a.settle)
     for _ in range(a.warmup):
         step()
@@ -301,7 +314,9 @@ def main(argv=None):
 
     # per-stage times through the individual entry points (same kernels, same stream)
     stages = {}
-    if not a.no_stages and masked:
+    if a.chunk_tokens:
+        pass                                # chunk pipeline: the layer time only
+    elif not a.no_stages and masked:
         stages = stage_times_masked(M, w, inp, weights, a.steps, cap)
     elif not a.no_stages and w.mode == "fp8" and w.route == "score":
         stages = stage_times(M, w, inp, weights, a.steps)
@@ -353,13 +368,16 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": (f"{w.name}{'_masked' if masked else ''}: T={w.T} d={w.d} "
                                 f"E={w.E} top-{w.k} I={w.I}"
-                                + (f", fixed-capacity layout C={cap}" if masked else "")),
+                                + (f", fixed-capacity layout C={cap}" if masked else "")
+                                + (f", two-stream pipeline of {a.chunk_tokens}-token chunks"
+                                   if a.chunk_tokens else "")),
                    "mode": w.mode, "route": w.route, "m_align": w.m_align,
                    "skew": f"+{w.skew_add} on {w.skew_frac:.0%} of experts" if w.skew_frac else None},
         "stages_ms": {k: round(v, 4) for k, v in stages.items()} or None,
         "roofline": roofline,
     }
-    if not a.no_cpu_baseline and w.mode == "fp8" and w.route == "score" and not masked:
+    if (not a.no_cpu_baseline and w.mode == "fp8" and w.route == "score" and not masked
+            and not a.chunk_tokens):
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)

@@ -24,6 +24,7 @@ __all__ = [
     "moe_quant_weight_fp8", "moe_pack_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_fp8_masked",
     "gemm_fp8", "grouped_gemm_w4a16",
     "grouped_gemm_f32", "moe_combine", "moe_layer_workspace_size", "moe_layer_fwd", "MoeError",
+    "moe_layer_chunked_workspace_size", "moe_layer_fwd_chunked",
     "LayerDesc",
 ]
 
@@ -342,3 +343,38 @@ def moe_layer_fwd(desc: LayerDesc, weights: dict, x: torch.Tensor,
                                      _ptr(y), _ptr(workspace), workspace.numel(), _ptr(counts),
                                      _stream(dev)), "moe_layer_fwd")
     return y, counts
+
+
+def moe_layer_chunked_workspace_size(desc: LayerDesc, chunk_tokens: int) -> int:
+    n = _lib_().moe_layer_chunked_workspace_size(C.byref(desc.c), chunk_tokens)
+    if n == 0:
+        raise MoeError(_lib.MOE_ERR_INVALID_ARG, "moe_layer_chunked_workspace_size",
+                       _lib_().moe_last_error().decode() or "chunked pipeline not available "
+                       "for this descriptor")
+    return n
+
+
+def moe_layer_fwd_chunked(desc: LayerDesc, weights: dict, x: torch.Tensor, chunk_tokens: int,
+                          token_ids: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          y: Optional[torch.Tensor] = None,
+                          aux_stream: Optional[torch.cuda.Stream] = None):
+    """The layer forward as a two-stream chunk pipeline (chunk i's routing, dispatch and
+    quantisation on ``aux_stream`` beside chunk i-1's GEMMs on the current stream).
+    Returns y."""
+    dev = x.device
+    if workspace is None:
+        workspace = torch.empty(moe_layer_chunked_workspace_size(desc, chunk_tokens),
+                                dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty(x.shape, dtype=x.dtype, device=dev)
+    if aux_stream is None:
+        aux_stream = torch.cuda.Stream(device=dev)
+    w = MoeLayerWeights(*(_ptr(weights.get(n)) for n in ("w_router", "bias", "w13", "s13", "w2",
+                                                        "s2")))
+    _lib.check(_lib_().moe_layer_fwd_chunked(C.byref(desc.c), C.byref(w), _ptr(x),
+                                             _ptr(token_ids), _ptr(y), _ptr(workspace),
+                                             workspace.numel(), chunk_tokens, _stream(dev),
+                                             C.c_void_p(aux_stream.cuda_stream)),
+               "moe_layer_fwd_chunked")
+    return y

@@ -553,110 +553,231 @@ size_t moe_layer_workspace_size(const moe_layer_desc* desc) {
   return layer_ws(desc).total;
 }
 
+namespace {
+
+// Device pointers of one layer pass inside a workspace region laid out by layer_ws.
+struct LayerPtrs {
+  float *logits, *part, *gw, *sx, *sh;
+  int32_t *idx, *counts, *offsets, *ros, *sor;
+  uint8_t *qx, *hq;
+  void* o;
+};
+
+LayerPtrs layer_ptrs(uint8_t* base, const LayerWs& L, int32_t* counts_out) {
+  LayerPtrs P;
+  P.logits = reinterpret_cast<float*>(base + L.logits);
+  P.part = reinterpret_cast<float*>(base + L.part);
+  P.idx = reinterpret_cast<int32_t*>(base + L.idx);
+  P.gw = reinterpret_cast<float*>(base + L.w);
+  P.counts = counts_out ? counts_out : reinterpret_cast<int32_t*>(base + L.counts);
+  P.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  P.ros = reinterpret_cast<int32_t*>(base + L.ros);
+  P.sor = reinterpret_cast<int32_t*>(base + L.sor);
+  P.qx = base + L.qx;
+  P.sx = reinterpret_cast<float*>(base + L.sx);
+  P.hq = base + L.h;
+  P.sh = reinterpret_cast<float*>(base + L.sh);
+  P.o = base + L.o;
+  return P;
+}
+
+int layer_args(const char* fn, const moe_layer_desc* d, const moe_layer_weights* w, const void* x,
+               const int64_t* token_ids, const void* y, const void* ws) {
+  int st = layer_check(d);
+  if (st) return st;
+  REQUIRE(w && x && y && ws, "%s: null pointer", fn);
+  REQUIRE(w->w13 && w->w2, "%s: null expert weights", fn);
+  if (d->mode != MOE_MODE_FP32) REQUIRE(w->s13 && w->s2, "%s: null weight scales", fn);
+  if (d->route == MOE_ROUTE_SCORE)
+    REQUIRE(w->w_router && w->bias, "%s: score routing needs w_router and bias", fn);
+  else
+    REQUIRE(token_ids, "%s: hash routing needs token_ids", fn);
+  return MOE_OK;
+}
+
+#define STEP(expr, what) \
+  if ((st = hip_status((expr), what))) return st;
+
+// route -> dispatch -> (FP8) token quantisation: everything before the expert GEMMs
+int layer_front(const moe_layer_desc* d, const moe_layer_weights* w, const void* x,
+                const int64_t* token_ids, const LayerPtrs& P, hipStream_t s) {
+  int st = MOE_OK;
+  const int T = d->T, D = d->d, E = d->E, k = d->k;
+  const int R = (int)layer_rows(d);
+  const bool f32 = d->mode == MOE_MODE_FP32;
+  const bool masked = d->layout == MOE_LAYOUT_MASKED;
+  if (d->route == MOE_ROUTE_SCORE) {
+    const int n_part = f32 ? 1 : moe::router_splits(T, D, E, true);
+    STEP(moe::launch_router(x, !f32, w->w_router, P.logits, T, D, E, P.part, n_part, s),
+         "router launch");
+    STEP(moe::launch_topk(P.logits, P.part, n_part, w->bias, T, E, k,
+                          d->route_flags & MOE_ROUTE_RENORM, P.idx, P.gw, s),
+         "topk launch");
+  } else {
+    STEP(moe::launch_hash_route(token_ids, T, E, P.idx, P.gw, s), "hash route launch");
+  }
+  const int cap = moe_capacity(T, k, E, d->capacity_factor);
+  if (cap < 0) return cap;
+  STEP(moe::launch_dispatch(P.idx, T, k, E, d->m_align, cap, P.counts,
+                            masked ? nullptr : P.offsets, P.ros, P.sor, R, s, masked),
+       "dispatch launch");
+  if (d->mode == MOE_MODE_FP8 && masked) {
+    // fixed-capacity layout: token codes gathered into [E, C, d], empty rows zero
+    STEP(moe::launch_quant_act(x, true, D, P.sor, k, R, P.qx, P.sx, s), "quant-gather launch");
+  } else if (d->mode == MOE_MODE_FP8) {
+    STEP(moe::launch_quant_act(x, true, D, nullptr, 1, T, P.qx, P.sx, s), "quant launch");
+  }
+  return MOE_OK;
+}
+
+// grouped GEMM1 (+ SwiGLU) -> grouped GEMM2 -> combine
+int layer_back(const moe_layer_desc* d, const moe_layer_weights* w, const void* x,
+               const LayerPtrs& P, void* y, int cus, hipStream_t s) {
+  int st = MOE_OK;
+  const int T = d->T, D = d->d, E = d->E, k = d->k, I = d->I;
+  const int R = (int)layer_rows(d);
+  const bool f32 = d->mode == MOE_MODE_FP32;
+  const bool masked = d->layout == MOE_LAYOUT_MASKED;
+  const double rows_per_group = (double)R / E;
+  if (d->mode == MOE_MODE_FP8 && masked) {
+    // both GEMMs over per-expert row counts clamped to C
+    const int cap = R / E;
+    STEP(moe::launch_gemm_fp8(P.qx, P.sx, nullptr, 1, static_cast<const uint8_t*>(w->w13),
+                              w->s13, P.counts, E, R, I, D, true, P.hq, P.sh, pick_bm(cap), cus,
+                              s, moe::kRowsMasked, cap),
+         "masked gemm1 launch");
+    STEP(moe::launch_gemm_fp8(P.hq, P.sh, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
+                              P.counts, E, R, D, I, false, P.o, nullptr, pick_bm(cap), cus, s,
+                              moe::kRowsMasked, cap),
+         "masked gemm2 launch");
+  } else if (d->mode == MOE_MODE_FP8) {
+    STEP(moe::launch_gemm_fp8(P.qx, P.sx, P.sor, k, static_cast<const uint8_t*>(w->w13), w->s13,
+                              P.offsets, E, R, I, D, true, P.hq, P.sh, pick_bm(rows_per_group),
+                              cus, s),
+         "gemm1 launch");
+    STEP(moe::launch_gemm_fp8(P.hq, P.sh, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
+                              P.offsets, E, R, D, I, false, P.o, nullptr,
+                              pick_bm(rows_per_group), cus, s),
+         "gemm2 launch");
+  } else if (d->mode == MOE_MODE_W4A16) {
+    uint16_t* h = reinterpret_cast<uint16_t*>(P.hq);
+    STEP(moe::launch_gemm_w4a16(static_cast<const uint16_t*>(x), P.sor, k,
+                                static_cast<const uint8_t*>(w->w13), w->s13, P.offsets, E, R, I,
+                                D, true, h, cus, s),
+         "gemm1 launch");
+    STEP(moe::launch_gemm_w4a16(h, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
+                                P.offsets, E, R, D, I, false, static_cast<uint16_t*>(P.o), cus,
+                                s),
+         "gemm2 launch");
+  } else {
+    float* h = reinterpret_cast<float*>(P.hq);
+    STEP(moe::launch_gemm_f32(static_cast<const float*>(x), P.sor, k,
+                              static_cast<const float*>(w->w13), P.offsets, E, R, I, D, true, h,
+                              s),
+         "gemm1 launch");
+    STEP(moe::launch_gemm_f32(h, nullptr, 1, static_cast<const float*>(w->w2), P.offsets, E, R,
+                              D, I, false, static_cast<float*>(P.o), s),
+         "gemm2 launch");
+  }
+  STEP(moe::launch_combine(P.o, !f32, P.ros, P.gw, T, k, D, y, !f32, s), "combine launch");
+  return MOE_OK;
+}
+
+#undef STEP
+
+// the descriptor of the token chunk [t0, t0 + n)
+moe_layer_desc chunk_desc(const moe_layer_desc* d, int n) {
+  moe_layer_desc c = *d;
+  c.T = n;
+  return c;
+}
+
+}  // namespace
+
 int moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* w, const void* x,
                   const int64_t* token_ids, void* y, void* ws, size_t ws_bytes, int32_t* counts_out,
                   void* stream) {
-  int st = layer_check(d);
+  int st = layer_args("moe_layer_fwd", d, w, x, token_ids, y, ws);
   if (st) return st;
-  REQUIRE(w && x && y && ws, "moe_layer_fwd: null pointer");
-  REQUIRE(w->w13 && w->w2, "moe_layer_fwd: null expert weights");
-  if (d->mode != MOE_MODE_FP32) REQUIRE(w->s13 && w->s2, "moe_layer_fwd: null weight scales");
-  if (d->route == MOE_ROUTE_SCORE)
-    REQUIRE(w->w_router && w->bias, "moe_layer_fwd: score routing needs w_router and bias");
-  else
-    REQUIRE(token_ids, "moe_layer_fwd: hash routing needs token_ids");
   const LayerWs L = layer_ws(d);
   if (ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_layer_fwd: workspace %zu < %zu bytes", ws_bytes, L.total);
   if (d->T == 0) return MOE_OK;
   int cus = 0;
   if ((st = current_device(&cus))) return st;
+  const LayerPtrs P = layer_ptrs(static_cast<uint8_t*>(ws), L, counts_out);
+  if ((st = layer_front(d, w, x, token_ids, P, S(stream)))) return st;
+  return layer_back(d, w, x, P, y, cus, S(stream));
+}
 
-  const hipStream_t s = S(stream);
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  float* logits = reinterpret_cast<float*>(base + L.logits);
-  int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
-  float* gw = reinterpret_cast<float*>(base + L.w);
-  int32_t* counts = counts_out ? counts_out : reinterpret_cast<int32_t*>(base + L.counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
-  int32_t* ros = reinterpret_cast<int32_t*>(base + L.ros);
-  int32_t* sor = reinterpret_cast<int32_t*>(base + L.sor);
-  const int T = d->T, D = d->d, E = d->E, k = d->k, I = d->I;
-  const int R = (int)layer_rows(d);
-  const bool f32 = d->mode == MOE_MODE_FP32;
-  const bool masked = d->layout == MOE_LAYOUT_MASKED;
+size_t moe_layer_chunked_workspace_size(const moe_layer_desc* desc, int chunk_tokens) {
+  if (layer_check(desc) != MOE_OK) return 0;
+  if (chunk_tokens < 1 || desc->capacity_factor > 0 || desc->layout != MOE_LAYOUT_CONTIGUOUS)
+    return 0;
+  const moe_layer_desc c = chunk_desc(desc, std::min(chunk_tokens, std::max(desc->T, 1)));
+  return 2 * align_up(layer_ws(&c).total);
+}
 
-#define STEP(expr, what) \
-  if ((st = hip_status((expr), what))) return st;
-
-  if (d->route == MOE_ROUTE_SCORE) {
-    const int n_part = f32 ? 1 : moe::router_splits(T, D, E, true);
-    float* part = reinterpret_cast<float*>(base + L.part);
-    STEP(moe::launch_router(x, !f32, w->w_router, logits, T, D, E, part, n_part, s),
-         "router launch");
-    STEP(moe::launch_topk(logits, part, n_part, w->bias, T, E, k,
-                          d->route_flags & MOE_ROUTE_RENORM, idx, gw, s),
-         "topk launch");
-  } else {
-    STEP(moe::launch_hash_route(token_ids, T, E, idx, gw, s), "hash route launch");
-  }
-  const int cap = moe_capacity(T, k, E, d->capacity_factor);
-  if (cap < 0) return cap;
-  STEP(moe::launch_dispatch(idx, T, k, E, d->m_align, cap, counts, masked ? nullptr : offsets,
-                            ros, sor, R, s, masked),
-       "dispatch launch");
-  const double rows_per_group = (double)R / E;
-  void* o = base + L.o;
-  if (d->mode == MOE_MODE_FP8 && masked) {
-    // fixed-capacity layout: token codes gathered into [E, C, d] (empty rows zero), then
-    // both GEMMs over per-expert row counts clamped to C
-    uint8_t* qa = base + L.qx;
-    float* sa = reinterpret_cast<float*>(base + L.sx);
-    uint8_t* hq = base + L.h;
-    float* sh = reinterpret_cast<float*>(base + L.sh);
-    STEP(moe::launch_quant_act(x, true, D, sor, k, R, qa, sa, s), "quant-gather launch");
-    STEP(moe::launch_gemm_fp8(qa, sa, nullptr, 1, static_cast<const uint8_t*>(w->w13), w->s13,
-                              counts, E, R, I, D, true, hq, sh, pick_bm(cap), cus, s,
-                              moe::kRowsMasked, cap),
-         "masked gemm1 launch");
-    STEP(moe::launch_gemm_fp8(hq, sh, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
-                              counts, E, R, D, I, false, o, nullptr, pick_bm(cap), cus, s,
-                              moe::kRowsMasked, cap),
-         "masked gemm2 launch");
-  } else if (d->mode == MOE_MODE_FP8) {
-    uint8_t* qx = base + L.qx;
-    float* sx = reinterpret_cast<float*>(base + L.sx);
-    uint8_t* hq = base + L.h;
-    float* sh = reinterpret_cast<float*>(base + L.sh);
-    STEP(moe::launch_quant_act(x, true, D, nullptr, 1, T, qx, sx, s), "quant launch");
-    STEP(moe::launch_gemm_fp8(qx, sx, sor, k, static_cast<const uint8_t*>(w->w13), w->s13, offsets,
-                              E, R, I, D, true, hq, sh, pick_bm(rows_per_group), cus, s),
-         "gemm1 launch");
-    STEP(moe::launch_gemm_fp8(hq, sh, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
-                              offsets, E, R, D, I, false, o, nullptr, pick_bm(rows_per_group),
-                              cus, s),
-         "gemm2 launch");
-  } else if (d->mode == MOE_MODE_W4A16) {
-    uint16_t* h = reinterpret_cast<uint16_t*>(base + L.h);
-    STEP(moe::launch_gemm_w4a16(static_cast<const uint16_t*>(x), sor, k,
-                                static_cast<const uint8_t*>(w->w13), w->s13, offsets, E, R, I, D,
-                                true, h, cus, s),
-         "gemm1 launch");
-    STEP(moe::launch_gemm_w4a16(h, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2, offsets,
-                                E, R, D, I, false, static_cast<uint16_t*>(o), cus, s),
-         "gemm2 launch");
-  } else {
-    float* h = reinterpret_cast<float*>(base + L.h);
-    STEP(moe::launch_gemm_f32(static_cast<const float*>(x), sor, k,
-                              static_cast<const float*>(w->w13), offsets, E, R, I, D, true, h, s),
-         "gemm1 launch");
-    STEP(moe::launch_gemm_f32(h, nullptr, 1, static_cast<const float*>(w->w2), offsets, E, R, D, I,
-                              false, static_cast<float*>(o), s),
-         "gemm2 launch");
-  }
-  STEP(moe::launch_combine(o, !f32, ros, gw, T, k, D, y, !f32, s), "combine launch");
-#undef STEP
-  return MOE_OK;
+int moe_layer_fwd_chunked(const moe_layer_desc* d, const moe_layer_weights* w, const void* x,
+                          const int64_t* token_ids, void* y, void* ws, size_t ws_bytes,
+                          int chunk_tokens, void* stream, void* stream_aux) {
+  int st = layer_args("moe_layer_fwd_chunked", d, w, x, token_ids, y, ws);
+  if (st) return st;
+  REQUIRE(chunk_tokens >= 1, "moe_layer_fwd_chunked: chunk_tokens must be >= 1");
+  REQUIRE(d->capacity_factor <= 0 && d->layout == MOE_LAYOUT_CONTIGUOUS,
+          "moe_layer_fwd_chunked: the chunked pipeline is dropless with the contiguous layout");
+  REQUIRE(stream != stream_aux, "moe_layer_fwd_chunked: stream_aux must differ from stream");
+  const size_t need = moe_layer_chunked_workspace_size(d, chunk_tokens);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_layer_fwd_chunked: workspace %zu < %zu bytes", ws_bytes,
+                need);
+  if (d->T == 0) return MOE_OK;
+  int cus = 0;
+  if ((st = current_device(&cus))) return st;
+  const hipStream_t sm = S(stream), sa = S(stream_aux);
+  const size_t region = need / 2;
+  const size_t xb = d->mode == MOE_MODE_FP32 ? 4 : 2;   // bytes per x / y element
+  // events: start (main -> aux), front[r] (aux -> main), back[r] (main -> aux), end.
+  // Created once per thread and device and reused: a wait already enqueued refers to the
+  // record before it, so a later call re-recording the same event does not disturb it.
+  int dev = 0;
+  if ((st = hip_status(hipGetDevice(&dev), "hipGetDevice"))) return st;
+  thread_local hipEvent_t ev_cache[kMaxDevices][6] = {};
+  hipEvent_t* ev = ev_cache[dev];
+  for (int i = 0; i < 6; ++i)
+    if (!ev[i] && (st = hip_status(hipEventCreateWithFlags(&ev[i], hipEventDisableTiming),
+                                   "event create")))
+      return st;
+  hipEvent_t ev_start = ev[0], ev_end = ev[1], ev_front[2] = {ev[2], ev[3]},
+             ev_back[2] = {ev[4], ev[5]};
+  auto run = [&]() -> int {
+    int s2 = MOE_OK;
+    // the aux stream starts after the caller's earlier work on the main stream
+    if ((s2 = hip_status(hipEventRecord(ev_start, sm), "event record"))) return s2;
+    if ((s2 = hip_status(hipStreamWaitEvent(sa, ev_start, 0), "stream wait"))) return s2;
+    const int nch = (d->T + chunk_tokens - 1) / chunk_tokens;
+    for (int i = 0; i < nch; ++i) {
+      const int t0 = i * chunk_tokens, n = std::min(chunk_tokens, d->T - t0), r = i & 1;
+      const moe_layer_desc c = chunk_desc(d, n);
+      const LayerWs L = layer_ws(&c);
+      const LayerPtrs P = layer_ptrs(static_cast<uint8_t*>(ws) + r * region, L, nullptr);
+      const void* xc = static_cast<const uint8_t*>(x) + (size_t)t0 * d->d * xb;
+      void* yc = static_cast<uint8_t*>(y) + (size_t)t0 * d->d * xb;
+      const int64_t* ids = token_ids ? token_ids + t0 : nullptr;
+      // region r was last read by chunk i-2's GEMMs and combine
+      if (i >= 2 && (s2 = hip_status(hipStreamWaitEvent(sa, ev_back[r], 0), "stream wait")))
+        return s2;
+      if ((s2 = layer_front(&c, w, xc, ids, P, sa))) return s2;
+      if ((s2 = hip_status(hipEventRecord(ev_front[r], sa), "event record"))) return s2;
+      if ((s2 = hip_status(hipStreamWaitEvent(sm, ev_front[r], 0), "stream wait"))) return s2;
+      if ((s2 = layer_back(&c, w, xc, P, yc, cus, sm))) return s2;
+      if ((s2 = hip_status(hipEventRecord(ev_back[r], sm), "event record"))) return s2;
+    }
+    // the caller's stream ends after everything either stream was given
+    if ((s2 = hip_status(hipEventRecord(ev_end, sa), "event record"))) return s2;
+    return hip_status(hipStreamWaitEvent(sm, ev_end, 0), "stream wait");
+  };
+  return run();
 }
 
 }  // extern "C"

@@ -316,6 +316,28 @@ int moe_layer_fwd(const moe_layer_desc *desc, const moe_layer_weights *w, const 
                   const int64_t *token_ids, void *y, void *ws, size_t ws_bytes,
                   int32_t *counts_out, void *stream);
 
+/* Bytes of device workspace moe_layer_fwd_chunked needs for `desc` and `chunk_tokens`
+ * (0 on a bad descriptor, a capacity, or the masked layout). */
+size_t moe_layer_chunked_workspace_size(const moe_layer_desc *desc, int chunk_tokens);
+
+/* The layer forward as a two-stream pipeline over token chunks (the chunked overlap of
+ * the MegaMoE walkthrough, discosf.com, sec. 2.3 and 4.3: 128- or 256-token chunks; the
+ * streams-and-events pattern of the Dense-to-TP-MoE article, cf-1.com, sec. 4.3): the
+ * batch is cut into chunks of `chunk_tokens` tokens (the last one ragged); chunk i's
+ * route, dispatch and token quantisation run on `stream_aux` while chunk i-1's expert
+ * GEMMs and combine run on `stream`, ordered by events, with two workspace regions
+ * alternating between chunks.  Each chunk is an independent layer pass, so y is the
+ * layer's output (routing per token does not depend on the chunking; the router's
+ * split-K order, and with it the last bits of the gate weights, may).  Every chunk
+ * streams the touched experts' weights again: on one GPU, where there is no all-to-all to
+ * hide, this costs about one weight stream per chunk.  Dropless contiguous layout only
+ * (capacity_factor <= 0).  stream_aux must differ from stream; it starts after the work
+ * enqueued on `stream` before the call, and `stream` ends after all of the call's work.
+ * counts are not reported.  Arguments otherwise as moe_layer_fwd. */
+int moe_layer_fwd_chunked(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                          const int64_t *token_ids, void *y, void *ws, size_t ws_bytes,
+                          int chunk_tokens, void *stream, void *stream_aux);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = _lib.load()
     declared = _declared()
-    assert len(declared) == 23, declared
+    assert len(declared) == 25, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -204,3 +204,24 @@ def test_masked_dispatch_and_layout_checks():
     bad = D(128, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 2.0, 16, 7)
     assert lib.moe_layer_workspace_size(C.byref(bad)) == 0
     assert "layout" in lib.moe_last_error().decode()
+
+
+def test_chunked_pipeline_checks():
+    lib = _lib.load()
+    D = _lib.MoeLayerDesc
+    d = D(4096, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.0, 16)
+    one = D(256, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.0, 16)
+    n = lib.moe_layer_chunked_workspace_size(C.byref(d), 256)
+    # two regions, each a whole layer pass over 256 tokens
+    assert n >= 2 * lib.moe_layer_workspace_size(C.byref(one))
+    assert lib.moe_layer_chunked_workspace_size(C.byref(d), 0) == 0
+    cap = D(4096, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 1.0, 16)
+    assert lib.moe_layer_chunked_workspace_size(C.byref(cap), 256) == 0
+    w = _lib.MoeLayerWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    S = C.c_void_p(0x10)
+    _err(lib.moe_layer_fwd_chunked(C.byref(d), C.byref(w), FAKE, None, FAKE, FAKE, n, 256, S, S),
+         "stream_aux")
+    _err(lib.moe_layer_fwd_chunked(C.byref(cap), C.byref(w), FAKE, None, FAKE, FAKE, n, 256, S,
+                                   None), "dropless")
+    _err(lib.moe_layer_fwd_chunked(C.byref(d), C.byref(w), FAKE, None, FAKE, FAKE, n, 0, S, None),
+         "chunk_tokens")

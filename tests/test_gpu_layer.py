@@ -164,3 +164,65 @@ def test_layer_masked_layout(cap_factor):
 def test_layer_small_w4a16_hash():
     run_layer_case(synth.Workload("small_w4a16", T=300, d=256, E=8, k=1, I=256, mode="w4a16",
                                   route="hash", m_align=64))
+
+
+# ------------------------------------------------------------ chunked pipeline
+
+def _near_tie_tokens(w, inp, margin):
+    if w.route != "score":
+        return np.zeros(w.T, bool)
+    logits = O.router_logits(inp["x"].float().numpy(), inp["w_router"].float().numpy())
+    return _near_ties(logits.astype(np.float32), inp["bias"].numpy(), w.k, margin)
+
+
+@pytest.mark.parametrize("mode,chunk", [("fp8", 128), ("fp8", 64), ("fp32", 100)])
+def test_layer_chunked_pipeline(mode, chunk):
+    """Two-stream chunk pipeline: every chunk an independent layer pass (the last ragged),
+    matched to the oracle's whole-batch layer."""
+    w = synth.Workload(f"chunked_{mode}", T=300, d=256, E=8, k=2, I=256, mode=mode,
+                       skew_frac=0.25, skew_add=2.0, m_align=16, seed=11)
+    note(f"chunked layer {mode} T={w.T} chunk={chunk}")
+    inp = synth.layer_inputs(w)
+    gw = _gpu_weights(w, inp)
+    desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, m_align=w.m_align)
+    x = inp["x"].to(dev())
+    y = M.moe_layer_fwd_chunked(desc, gw, x, chunk)
+    y1, _ = M.moe_layer_fwd(desc, gw, x)
+    staged = staged_fp8_layer(M, w.T, w.E, w.k, w.I, w.m_align, x, gw) if mode == "fp8" else None
+    torch.cuda.synchronize()
+    ref = O.layer_forward(w.mode, inp["x"].float().numpy(), E=w.E, k=w.k, I=w.I,
+                          m_align=w.m_align, w_router=inp["w_router"].float().numpy(),
+                          bias=inp["bias"].numpy(), experts=_oracle_experts(w, inp),
+                          keep=(mode == "fp8"))
+    amb = _near_tie_tokens(w, inp, 1e-4)
+    keep = np.nonzero(~amb)[0]
+    yg = to_np(y).astype(np.float64)
+    # against the single pass: the same experts' rows; only the gate weights' last bits
+    # (the router's split-K order depends on the chunk size) may differ
+    d1 = np.abs(yg[keep] - to_np(y1).astype(np.float64)[keep]).max()
+    print(f"chunked vs single pass: max |diff| {d1:.3e}, near-tie tokens {int(amb.sum())}")
+    if mode == "fp32":
+        beyond, raw = error_ratios(yg[keep], ref["y"][keep], rounding=0.0)
+        print(f"raw={raw:.3e}")
+        assert raw <= TOL
+        return
+    h_gpu = gpu_h_by_slot(staged, [t * w.k + j for t in keep for j in range(w.k)])
+    e = fp8_layer_errors(yg[keep], ref, keep, w.T, w.k, h_gpu)
+    print(f"errors {e}")
+    assert e["beyond_flip"] <= TOL and e["beyond_noflip"] <= TOL
+
+
+def test_layer_chunked_pipeline_hash_bitexact():
+    """Hash routing has no logits: the chunk pipeline then gives the single pass's output
+    bit for bit (the same expert rows, summed in the same order)."""
+    w = synth.Workload("chunked_w4a16", T=300, d=256, E=8, k=1, I=256, mode="w4a16",
+                       route="hash", m_align=64)
+    note(f"chunked layer w4a16 hash T={w.T} chunk=128")
+    inp = synth.layer_inputs(w)
+    gw = _gpu_weights(w, inp)
+    desc = M.LayerDesc(w.T, w.d, w.E, w.k, w.I, mode=w.mode, route="hash", m_align=w.m_align)
+    x, ids = inp["x"].to(dev()), inp["token_ids"].to(dev())
+    y = M.moe_layer_fwd_chunked(desc, gw, x, 128, token_ids=ids)
+    y1, _ = M.moe_layer_fwd(desc, gw, x, ids)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1)
