@@ -52,6 +52,10 @@ def make_layer(w: synth.Workload, dev):
     elif w.mode == "w4a16":
         weights["w13"], weights["s13"] = M.moe_quant_weight_int4(inp["w13"])
         weights["w2"], weights["s2"] = M.moe_quant_weight_int4(inp["w2"])
+    elif w.mode == "w4a8":
+        # 4-bit codes and scales rearranged once, offline, into the order the GEMM loads
+        weights["w13"], weights["s13"] = M.moe_pack_weight_int4(*M.moe_quant_weight_int4(inp["w13"]))
+        weights["w2"], weights["s2"] = M.moe_pack_weight_int4(*M.moe_quant_weight_int4(inp["w2"]))
     else:
         weights["w13"], weights["w2"] = inp["w13"], inp["w2"]
     return inp, weights
@@ -75,6 +79,12 @@ def gemm_bytes_flops(w: synth.Workload, counts: np.ndarray):
         wb2 = d * I // 2 + d * (I // 128) * 4
         a1 = w.T * d * 2
         h = R * I * 2
+        o = R * d * 2
+    elif w.mode == "w4a8":
+        wb13 = 2 * I * d // 2 + 2 * I * (d // 128) * 4
+        wb2 = d * I // 2 + d * (I // 128) * 4
+        a1 = w.T * d + w.T * (d // 128) * 4
+        h = R * I + R * (I // 128) * 4
         o = R * d * 2
     else:
         wb13, wb2 = 2 * I * d * 4, d * I * 4
@@ -322,6 +332,8 @@ def main(argv=None):
         stages = stage_times(M, w, inp, weights, a.steps)
     elif not a.no_stages and w.mode == "w4a16" and w.route == "hash":
         stages = stage_times_w4a16(M, w, inp, weights, a.steps)
+    elif not a.no_stages and w.mode == "w4a8" and w.route == "hash":
+        stages = stage_times_w4a8(M, w, inp, weights, a.steps)
     if stages:
         log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
     g1_ms = stages.get("gemm1")
@@ -334,6 +346,16 @@ def main(argv=None):
         roofline = {"kernel": "grouped_gemm_w4a16 (GEMM1: gate+up, SwiGLU)",
                     "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None, "avg_ms": round(g1_ms, 4),
+                    "hbm_gbs": round(g["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9, 1),
+                    "flops_per_launch": g["gemm1_flops"]}
+    elif g1_ms and w.mode == "w4a8":
+        # 4-bit weights (~860 FLOP per weight byte at this shape) on the FP8 matrix core:
+        # the bound is the FP8 MFMA peak
+        tf = g["gemm1_flops"] / (g1_ms * 1e-3) / 1e12
+        roofline = {"kernel": "grouped_gemm_w4a8 (GEMM1: gate+up, SwiGLU, e4m3 requant)",
+                    "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
                     "traffic": None, "avg_ms": round(g1_ms, 4),
                     "hbm_gbs": round(g["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9, 1),
                     "flops_per_launch": g["gemm1_flops"]}
@@ -364,7 +386,8 @@ def main(argv=None):
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "layer_hbm_frac": round(bytes_ / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"fp8": "e4m3", "w4a16": "int4xbf16", "fp32": "f32"}[w.mode],
+        "dtype": {"fp8": "e4m3", "w4a16": "int4xbf16", "w4a8": "int4xe4m3",
+                  "fp32": "f32"}[w.mode],
         "data": "synthetic",
         "config": {"workload": (f"{w.name}{'_masked' if masked else ''}: T={w.T} d={w.d} "
                                 f"E={w.E} top-{w.k} I={w.I}"
@@ -610,6 +633,38 @@ def stage_times_masked(M, w, inp, weights, steps, cap):
                                            w.I, swiglu=True)
         ev[4].record()
         o = M.grouped_gemm_fp8_masked(hq, sh, weights["w2"], weights["s2"], counts, cap, w.d)
+        ev[5].record()
+        M.moe_combine(o, ros, gw, w.T, w.k)
+        ev[6].record()
+        torch.cuda.synchronize()
+        if it == 0:
+            continue
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    return {n: acc[n] / steps for n in names}
+
+
+def stage_times_w4a8(M, w, inp, weights, steps):
+    """Stage times of the hash-routed layer with 4-bit weights on the FP8 matrix core:
+    route_hash -> dispatch -> 1x128 quant -> GEMM1 with the token gather -> GEMM2 ->
+    combine."""
+    x = inp["x"]
+    names = ["route", "dispatch", "quant", "gemm1", "gemm2", "combine"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = {n: 0.0 for n in names}
+    R = M.moe_rows_bound(w.T, w.k, w.E, w.m_align)
+    for it in range(steps + 1):
+        ev[0].record()
+        idx, gw = M.moe_route_hash(inp["token_ids"], w.E)
+        ev[1].record()
+        counts, offsets, ros, sor = M.moe_dispatch(idx, w.E, w.m_align)
+        ev[2].record()
+        qx, sx = M.moe_quant_fp8(x)
+        ev[3].record()
+        hq, sh = M.grouped_gemm_w4a8(qx, sx, weights["w13"], weights["s13"], offsets, R, w.I,
+                                     swiglu=True, a_rows=sor, a_row_div=w.k)
+        ev[4].record()
+        o = M.grouped_gemm_w4a8(hq, sh, weights["w2"], weights["s2"], offsets, R, w.d)
         ev[5].record()
         M.moe_combine(o, ros, gw, w.T, w.k)
         ev[6].record()

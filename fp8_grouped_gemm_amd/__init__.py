@@ -14,14 +14,15 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_BF16, MOE_E4M3, MOE_EPI_PLAIN, MOE_EPI_SWIGLU, MOE_F32, MOE_INT4,
-                   MOE_MODE_FP32, MOE_MODE_FP8, MOE_MODE_W4A16, MOE_ROUTE_HASH,
+                   MOE_MODE_FP32, MOE_MODE_FP8, MOE_MODE_W4A16, MOE_MODE_W4A8, MOE_ROUTE_HASH,
                    MOE_ROUTE_RENORM, MOE_ROUTE_SCORE, MoeError, MoeLayerDesc, MoeLayerWeights)
 
 __all__ = [
     "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route", "moe_route_noalloc",
     "moe_route_from_logits", "moe_route_hash", "moe_route_workspace_size", "moe_dispatch",
     "moe_dispatch_masked", "moe_quant_fp8",
-    "moe_quant_weight_fp8", "moe_pack_weight_fp8", "moe_quant_weight_int4", "grouped_gemm_fp8", "grouped_gemm_fp8_masked",
+    "moe_quant_weight_fp8", "moe_pack_weight_fp8", "moe_quant_weight_int4", "moe_pack_weight_int4",
+    "grouped_gemm_fp8", "grouped_gemm_fp8_masked", "grouped_gemm_w4a8",
     "gemm_fp8", "grouped_gemm_w4a16",
     "grouped_gemm_f32", "moe_combine", "moe_layer_workspace_size", "moe_layer_fwd", "MoeError",
     "moe_layer_chunked_workspace_size", "moe_layer_fwd_chunked",
@@ -210,6 +211,17 @@ def moe_quant_weight_int4(w: torch.Tensor):
     return q, s
 
 
+def moe_pack_weight_int4(q: torch.Tensor, s7: torch.Tensor):
+    """int4 codes [G, N, K/2] + scales [G, N, K/128] (moe_quant_weight_int4) -> the
+    fragment-major order grouped_gemm_w4a8 reads (same shapes and byte counts)."""
+    G, N, K2 = q.shape
+    qf = torch.empty_like(q)
+    s7f = torch.empty_like(s7)
+    _lib.check(_lib_().moe_pack_weight_int4(_ptr(q), _ptr(s7), G, N, 2 * K2, _ptr(qf), _ptr(s7f),
+                                            _stream(q.device)), "moe_pack_weight_int4")
+    return qf, s7f
+
+
 # --------------------------------------------------------------- grouped GEMM
 
 def grouped_gemm_fp8(A, sA, B, sB, offsets, R_cap: int, N: int, swiglu: bool = False,
@@ -230,6 +242,27 @@ def grouped_gemm_fp8(A, sA, B, sB, offsets, R_cap: int, N: int, swiglu: bool = F
     _lib.check(_lib_().grouped_gemm_fp8(_ptr(A), _ptr(sA), _ptr(a_rows), a_row_div, _ptr(B),
                                         _ptr(sB), _ptr(offsets), G, R_cap, N, K, epi, out_dt,
                                         _ptr(Cc), _ptr(sC), _stream(dev)), "grouped_gemm_fp8")
+    return (Cc, sC) if swiglu else Cc
+
+
+def grouped_gemm_w4a8(A, sA, B, s7, offsets, R_cap: int, N: int, swiglu: bool = False,
+                      a_rows: Optional[torch.Tensor] = None, a_row_div: int = 1):
+    """4-bit weights (packed by moe_pack_weight_int4) on the FP8 matrix core.  Returns C bf16
+    [R_cap, N] (plain) or (codes e4m3 [R_cap, N], sC [R_cap, N/128])."""
+    K = A.shape[1]
+    G = B.shape[0]
+    dev = A.device
+    if swiglu:
+        Cc = torch.empty((R_cap, N), dtype=torch.uint8, device=dev)
+        sC = torch.empty((R_cap, N // 128), dtype=torch.float32, device=dev)
+        out_dt, epi = MOE_E4M3, MOE_EPI_SWIGLU
+    else:
+        Cc = torch.empty((R_cap, N), dtype=torch.bfloat16, device=dev)
+        sC = None
+        out_dt, epi = MOE_BF16, MOE_EPI_PLAIN
+    _lib.check(_lib_().grouped_gemm_w4a8(_ptr(A), _ptr(sA), _ptr(a_rows), a_row_div, _ptr(B),
+                                         _ptr(s7), _ptr(offsets), G, R_cap, N, K, epi, out_dt,
+                                         _ptr(Cc), _ptr(sC), _stream(dev)), "grouped_gemm_w4a8")
     return (Cc, sC) if swiglu else Cc
 
 
@@ -308,7 +341,8 @@ class LayerDesc:
 
     def __init__(self, T, d, E, k, I, mode="fp8", route="score", renorm=False,
                  capacity_factor=0.0, m_align=128, layout="contiguous"):
-        modes = {"fp32": MOE_MODE_FP32, "fp8": MOE_MODE_FP8, "w4a16": MOE_MODE_W4A16}
+        modes = {"fp32": MOE_MODE_FP32, "fp8": MOE_MODE_FP8, "w4a16": MOE_MODE_W4A16,
+                 "w4a8": MOE_MODE_W4A8}
         layouts = {"contiguous": _lib.MOE_LAYOUT_CONTIGUOUS, "masked": _lib.MOE_LAYOUT_MASKED}
         self.c = MoeLayerDesc(T, d, E, k, I, modes[mode],
                               MOE_ROUTE_HASH if route == "hash" else MOE_ROUTE_SCORE,

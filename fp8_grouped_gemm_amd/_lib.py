@@ -19,7 +19,7 @@ MOE_ERR_WORKSPACE = -4
 MOE_F32, MOE_BF16, MOE_E4M3, MOE_INT4 = 0, 1, 2, 3
 MOE_ROUTE_RENORM = 1
 MOE_EPI_PLAIN, MOE_EPI_SWIGLU = 0, 1
-MOE_MODE_FP32, MOE_MODE_FP8, MOE_MODE_W4A16 = 0, 1, 2
+MOE_MODE_FP32, MOE_MODE_FP8, MOE_MODE_W4A16, MOE_MODE_W4A8 = 0, 1, 2, 3
 MOE_ROUTE_SCORE, MOE_ROUTE_HASH = 0, 1
 MOE_LAYOUT_CONTIGUOUS, MOE_LAYOUT_MASKED = 0, 1
 
@@ -62,6 +62,8 @@ SIGNATURES = {
     "grouped_gemm_fp8_masked": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "gemm_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
     "grouped_gemm_w4a16": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_pack_weight_int4": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+    "grouped_gemm_w4a8": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "grouped_gemm_f32": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_layer_workspace_size": (_Z, [C.POINTER(MoeLayerDesc)]),

@@ -11,6 +11,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,6 +35,7 @@ FILE_FLAGS = {
     # FP8 GEMM: MFMA results in VGPRs, so the per-block promotion FMAs read them without
     # accvgpr moves
     "gemm_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm_w4a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
@@ -42,15 +44,40 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
+def scratch_users(remarks: str) -> list:
+    """Kernels the compiler's resource remarks report with private (scratch) memory.
+
+    Several kernels (the GEMMs, the router) wait for their own global->LDS copies by
+    counting this wave's outstanding vector memory operations (s_waitcnt vmcnt with a
+    fixed count).  Register spills add scratch loads and stores to that count, and the
+    wait would then release before the copy landed, so a spilling kernel is a build
+    error rather than a slowdown."""
+    users, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            users.append(f"{name} ({m.group(1)} bytes/lane)")
+    return users
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-x", "hip", "-c", src,
-           "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []),
+           "-Rpass-analysis=kernel-resource-usage", "-x", "hip", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    spills = scratch_users(r.stderr)
+    if spills:
+        os.remove(obj)
+        raise RuntimeError(f"{src}: kernels use scratch memory (register spills), which "
+                           f"breaks their counted memory waits: {', '.join(spills)}")
     return obj
 
 

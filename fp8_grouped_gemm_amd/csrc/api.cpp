@@ -388,6 +388,49 @@ int grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B,
                     "grouped_gemm_fp8_masked launch");
 }
 
+int moe_pack_weight_int4(const uint8_t* q, const float* s7, int G, int N, int K, uint8_t* qf,
+                         float* s7f, void* stream) {
+  REQUIRE(q && s7 && qf && s7f, "moe_pack_weight_int4: null pointer");
+  REQUIRE(q != qf && (const void*)s7 != (const void*)s7f,
+          "moe_pack_weight_int4: outputs must not overlap inputs");
+  REQUIRE(G >= 1 && G <= 65535, "moe_pack_weight_int4: G must be in [1, 65535]");
+  REQUIRE(N > 0 && K > 0 && N % 128 == 0 && K % 128 == 0,
+          "moe_pack_weight_int4: N and K must be positive multiples of 128 (got %d, %d)", N, K);
+  int st = current_device(nullptr);
+  if (st) return st;
+  return hip_status(moe::launch_pack_weight_int4(q, s7, G, N, K, qf, s7f, S(stream)),
+                    "int4 pack launch");
+}
+
+int grouped_gemm_w4a8(const uint8_t* A, const float* sA, const int32_t* a_rows, int a_row_div,
+                      const uint8_t* B, const float* s7, const int32_t* offsets, int G, int R_cap,
+                      int N, int K, int epilogue, moe_dtype out_dt, void* C, float* sC,
+                      void* stream) {
+  int st = v_gemm_common(A, B, offsets, G, R_cap, N, K, epilogue, C);
+  if (st) return st;
+  REQUIRE(sA && s7, "grouped_gemm_w4a8: null scale pointer");
+  REQUIRE(N % 128 == 0 && K % 128 == 0, "grouped_gemm_w4a8: N and K must be multiples of 128");
+  REQUIRE(K / 128 <= moe::kGemmMaxKBlocks, "grouped_gemm_w4a8: K must be <= %d",
+          128 * moe::kGemmMaxKBlocks);
+  REQUIRE(a_row_div >= 1, "grouped_gemm_w4a8: a_row_div must be >= 1");
+  const bool swiglu = epilogue == MOE_EPI_SWIGLU;
+  if (swiglu) {
+    REQUIRE(out_dt == MOE_E4M3 && sC, "grouped_gemm_w4a8: SwiGLU epilogue writes e4m3 + sC");
+  } else {
+    REQUIRE(out_dt == MOE_BF16, "grouped_gemm_w4a8: plain epilogue writes bf16");
+  }
+  REQUIRE(a_rows || (long long)R_cap * K <= kMaxOperandBytes,
+          "grouped_gemm_w4a8: R_cap * K = %lld exceeds the 32-bit operand offset range",
+          (long long)R_cap * K);
+  if (R_cap == 0) return MOE_OK;
+  int cus = 0;
+  if ((st = current_device(&cus))) return st;
+  return hip_status(moe::launch_gemm_w4a8(A, sA, a_rows, a_row_div, B, s7, offsets, G, R_cap, N,
+                                          K, swiglu, C, sC, pick_bm((double)R_cap / G), cus,
+                                          S(stream)),
+                    "grouped_gemm_w4a8 launch");
+}
+
 int gemm_fp8(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB, int M, int N,
              int K, uint16_t* C, void* stream) {
   REQUIRE(B && sB && (M == 0 || (A && sA && C)), "gemm_fp8: null pointer");
@@ -467,7 +510,8 @@ int layer_check(const moe_layer_desc* d) {
   REQUIRE(d->T >= 0 && d->d >= 128 && d->E >= 1 && d->E <= 1024 && d->k >= 1 && d->I >= 1,
           "moe_layer: bad sizes T=%d d=%d E=%d k=%d I=%d", d->T, d->d, d->E, d->k, d->I);
   REQUIRE(d->k <= d->E && d->k <= 64, "moe_layer: k must be <= min(E, 64)");
-  REQUIRE(d->mode == MOE_MODE_FP32 || d->mode == MOE_MODE_FP8 || d->mode == MOE_MODE_W4A16,
+  REQUIRE(d->mode == MOE_MODE_FP32 || d->mode == MOE_MODE_FP8 || d->mode == MOE_MODE_W4A16 ||
+              d->mode == MOE_MODE_W4A8,
           "moe_layer: unknown mode %d", d->mode);
   REQUIRE(d->route == MOE_ROUTE_SCORE || d->route == MOE_ROUTE_HASH, "moe_layer: unknown route %d",
           d->route);
@@ -478,12 +522,12 @@ int layer_check(const moe_layer_desc* d) {
   REQUIRE(std::isfinite(d->capacity_factor), "moe_layer: capacity_factor must be finite");
   REQUIRE(d->m_align >= 1 && d->m_align <= 1024, "moe_layer: m_align must be in [1, 1024]");
   REQUIRE(d->d % 128 == 0, "moe_layer: d must be a multiple of 128");
-  if (d->mode == MOE_MODE_FP8) {
+  if (d->mode == MOE_MODE_FP8 || d->mode == MOE_MODE_W4A8) {
     REQUIRE(d->I % 128 == 0, "moe_layer: fp8 needs I %% 128 == 0");
     REQUIRE(d->d <= 128 * moe::kGemmMaxKBlocks && d->I <= 128 * moe::kGemmMaxKBlocks,
             "moe_layer: fp8 needs d, I <= %d", 128 * moe::kGemmMaxKBlocks);
   }
-  if (d->mode == MOE_MODE_FP8) {
+  if (d->mode == MOE_MODE_FP8 || d->mode == MOE_MODE_W4A8) {
     // GEMM1 reads the token codes [T, d], GEMM2 the h codes [R, I] with 32-bit offsets
     const long long R = (long long)d->T * d->k + (long long)d->E * (d->m_align - 1);
     REQUIRE((long long)d->T * d->d <= kMaxOperandBytes && R * d->I <= kMaxOperandBytes,
@@ -519,6 +563,7 @@ LayerWs layer_ws(const moe_layer_desc* d) {
   const bool masked = d->layout == MOE_LAYOUT_MASKED;
   size_t p = 0;
   auto take = [&](size_t bytes) { size_t at = p; p = align_up(p + bytes); return at; };
+  const bool q8 = d->mode == MOE_MODE_FP8 || d->mode == MOE_MODE_W4A8;
   L.part = take(d->route == MOE_ROUTE_SCORE && d->mode != MOE_MODE_FP32
                     ? moe_route_workspace_size(d->T, d->d, d->E, MOE_BF16) : 0);
   L.logits = take(d->route == MOE_ROUTE_SCORE ? T * E * 4 : 0);
@@ -528,7 +573,7 @@ LayerWs layer_ws(const moe_layer_desc* d) {
   L.offsets = take((E + 1) * 4);
   L.ros = take(T * k * 4);
   L.sor = take(R * 4);
-  if (d->mode == MOE_MODE_FP8) {
+  if (q8) {
     // masked: the expert-row buffer [E, C, d] of gathered token codes
     L.qx = take((masked ? R : T) * D);
     L.sx = take((masked ? R : T) * (D / 128) * 4);
@@ -624,7 +669,7 @@ int layer_front(const moe_layer_desc* d, const moe_layer_weights* w, const void*
   if (d->mode == MOE_MODE_FP8 && masked) {
     // fixed-capacity layout: token codes gathered into [E, C, d], empty rows zero
     STEP(moe::launch_quant_act(x, true, D, P.sor, k, R, P.qx, P.sx, s), "quant-gather launch");
-  } else if (d->mode == MOE_MODE_FP8) {
+  } else if (d->mode == MOE_MODE_FP8 || d->mode == MOE_MODE_W4A8) {
     STEP(moe::launch_quant_act(x, true, D, nullptr, 1, T, P.qx, P.sx, s), "quant launch");
   }
   return MOE_OK;
@@ -659,6 +704,15 @@ int layer_back(const moe_layer_desc* d, const moe_layer_weights* w, const void* 
                               P.offsets, E, R, D, I, false, P.o, nullptr,
                               pick_bm(rows_per_group), cus, s),
          "gemm2 launch");
+  } else if (d->mode == MOE_MODE_W4A8) {
+    STEP(moe::launch_gemm_w4a8(P.qx, P.sx, P.sor, k, static_cast<const uint8_t*>(w->w13), w->s13,
+                               P.offsets, E, R, I, D, true, P.hq, P.sh, pick_bm(rows_per_group),
+                               cus, s),
+         "w4a8 gemm1 launch");
+    STEP(moe::launch_gemm_w4a8(P.hq, P.sh, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
+                               P.offsets, E, R, D, I, false, P.o, nullptr,
+                               pick_bm(rows_per_group), cus, s),
+         "w4a8 gemm2 launch");
   } else if (d->mode == MOE_MODE_W4A16) {
     uint16_t* h = reinterpret_cast<uint16_t*>(P.hq);
     STEP(moe::launch_gemm_w4a16(static_cast<const uint16_t*>(x), P.sor, k,

@@ -43,6 +43,16 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_r
                            const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
                            void* C, float* sC, int bm, int num_cus, hipStream_t s,
                            int rows_mode = 0, int cap = 0);
+// int4 codes [G][R][K/2] and scales [G][R][K/128] -> the fragment-major order the W4A8
+// GEMM loads: codes [G][R/16][K/128][64][16 B], scales [G][R/16][K/128][16]
+hipError_t launch_pack_weight_int4(const uint8_t* q, const float* s7, int G, int R, int K,
+                                   uint8_t* qf, float* s7f, hipStream_t s);
+// the FP8 GEMM with packed 4-bit weights (W4A8); arguments as launch_gemm_fp8
+hipError_t launch_gemm_w4a8(const uint8_t* A, const float* sA, const int32_t* a_rows,
+                            int a_row_div, const uint8_t* Bf, const float* s7f,
+                            const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
+                            void* C, float* sC, int bm, int num_cus, hipStream_t s,
+                            int rows_mode = 0, int cap = 0);
 hipError_t launch_gemm_w4a16(const uint16_t* A, const int32_t* a_rows, int a_row_div,
                              const uint8_t* B, const float* s7, const int32_t* offsets, int G,
                              int R_cap, int N, int K, bool swiglu, uint16_t* C, int num_cus,

@@ -67,6 +67,8 @@ typedef enum {
 #define MOE_MODE_FP32 0   /* fp32 activations and weights, no quantisation            */
 #define MOE_MODE_FP8 1    /* e4m3 weights with 128x128 scales, 1x128 activation quant */
 #define MOE_MODE_W4A16 2  /* int4 weights with 1x128 per-channel scales, bf16 acts    */
+#define MOE_MODE_W4A8 3   /* int4 weights, 1x128 per-channel scales, on the FP8 MFMA  */
+                          /* with 1x128 e4m3 activations (moe_pack_weight_int4)     */
 #define MOE_LAYOUT_CONTIGUOUS 0 /* expert rows concatenated, each padded to m_align   */
 #define MOE_LAYOUT_MASKED 1     /* fixed capacity: expert e owns rows [e C, e C + C)    */
 #define MOE_ROUTE_SCORE 0 /* biased softmax top-k over router logits                  */
@@ -244,6 +246,30 @@ int grouped_gemm_fp8_masked(const uint8_t *A, const float *sA, const uint8_t *B,
 int gemm_fp8(const uint8_t *A, const float *sA, const uint8_t *B, const float *sB, int M,
              int N, int K, uint16_t *C, void *stream);
 
+/* Rearranges int4 weights (codes q [G, N, K/2] and scales s7 [G, N, K/128] as
+ * moe_quant_weight_int4 writes them) into the fragment-major order grouped_gemm_w4a8
+ * loads: qf [G][N/16][K/128][64][16 B], lane l of 16-row block nb and 128-deep block kb
+ * holding the 32 codes of row 16 nb + (l mod 16), k = 128 kb + 32 (l div 16) .. +32
+ * (bytes 64 kb + 16 (l div 16) .. +16 of that row); s7f [G][N/16][K/128][16], the
+ * scales of a block's 16 rows together.  A pure permutation, done once per weight.
+ * Outputs must not overlap inputs; N and K multiples of 128.  (Layout of this library,
+ * not of the pages.) */
+int moe_pack_weight_int4(const uint8_t *q, const float *s7, int G, int N, int K, uint8_t *qf,
+                         float *s7f, void *stream);
+
+/* Grouped GEMM with 4-bit weights on the FP8 matrix core (W4A8).  The weights are the
+ * block-wise 4-bit codes of the DeepSeek-V4 lecture (tqpw.cn sec. 3.1: q = round(w /
+ * max|w| * 7) in [-7, 7] per output channel and 128-wide K block, s7 = max|w| / 7), kept
+ * 4-bit in memory and fed to the e4m3 matrix instruction, on which the integers -7..7
+ * are exact; the activations are 1x128 e4m3 as in grouped_gemm_fp8.  Each 128-deep block
+ * is promoted as acc += sA[a, kb] * s7[g, n, kb] * partial (two-level accumulation,
+ * qidao123.com day 3).  B and s7 as packed by moe_pack_weight_int4 ([G, Nb, K] logical,
+ * Nb = N or 2N for SwiGLU); every other argument, output and limit as grouped_gemm_fp8. */
+int grouped_gemm_w4a8(const uint8_t *A, const float *sA, const int32_t *a_rows, int a_row_div,
+                      const uint8_t *B, const float *s7, const int32_t *offsets, int G,
+                      int R_cap, int N, int K, int epilogue, moe_dtype out_dt, void *C,
+                      float *sC, void *stream);
+
 /* Grouped GEMM with int4 weights and bf16 activations (block-wise 4-bit expert weights
  * with max-abs scales, DeepSeek-V4 lecture, tqpw.cn, sec. 3.1; groups as in the
  * MegaMoE walkthrough, discosf.com, sec. 3.2): B codes [G, Nb, K/2] and
@@ -287,10 +313,11 @@ typedef struct {
   const float *bias;       /* [E] fp32 (score routing)                              */
   const void *w13;         /* [E, 2I, d]: rows [0,I) gate, [I,2I) up.  fp32 | e4m3  */
                            /*   fragment-major (moe_pack_weight_fp8) | int4 packed    */
-                           /*   [E, 2I, d/2]                                         */
-  const float *s13;        /* FP8: [E, 2I/128, d/128]; W4A16: [E, 2I, d/128]        */
+                           /*   [E, 2I, d/2] (W4A8: moe_pack_weight_int4 order)       */
+  const float *s13;        /* FP8: [E, 2I/128, d/128]; W4A16: [E, 2I, d/128];       */
+                           /*   W4A8: packed by moe_pack_weight_int4                */
   const void *w2;          /* [E, d, I] (e4m3: fragment-major; int4: [E, d, I/2])   */
-  const float *s2;         /* FP8: [E, d/128, I/128]; W4A16: [E, d, I/128]          */
+  const float *s2;         /* FP8: [E, d/128, I/128]; W4A16: [E, d, I/128]; W4A8    */
 } moe_layer_weights;
 
 /* Bytes of device workspace moe_layer_fwd needs for `desc` (0 on a bad descriptor;

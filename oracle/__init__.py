@@ -23,15 +23,16 @@ Functions whose result no test pins to an independent fact say "parity
 unpinned" in their docstring.
 """
 from .codecs import (E4M3_MAX, bf16_round, e4m3_decode, e4m3_decode_table, e4m3_encode,
-                     int4_dequant, int4_quant_rows, quant_fp8_act, quant_fp8_weight,
+                     int4_dequant, int4_dequant_exact, int4_quant_rows, quant_fp8_act,
+                     quant_fp8_weight,
                      dequant_fp8_act, dequant_fp8_weight)
-from .moe import (capacity, combine, dispatch, dispatch_masked, grouped_gemm, grouped_gemm_fp8, hash_route,
+from .moe import (capacity, combine, dispatch, dispatch_masked, grouped_gemm, grouped_gemm_w4a8, grouped_gemm_fp8, hash_route,
                   layer_forward, router_logits, rows_bound, silu, swiglu, topk_route)
 
 __all__ = [
     "E4M3_MAX", "bf16_round", "e4m3_decode", "e4m3_decode_table", "e4m3_encode",
-    "int4_dequant", "int4_quant_rows", "quant_fp8_act", "quant_fp8_weight",
+    "int4_dequant", "int4_dequant_exact", "int4_quant_rows", "quant_fp8_act", "quant_fp8_weight",
     "dequant_fp8_act", "dequant_fp8_weight", "capacity", "combine", "dispatch", "dispatch_masked",
-    "grouped_gemm", "grouped_gemm_fp8", "hash_route", "layer_forward", "router_logits",
+    "grouped_gemm", "grouped_gemm_fp8", "grouped_gemm_w4a8", "hash_route", "layer_forward", "router_logits",
     "rows_bound", "silu", "swiglu", "topk_route",
 ]

@@ -187,6 +187,16 @@ def int4_dequant(q, s7) -> np.ndarray:
     return bf16_round(prod).reshape(G, N, K)
 
 
+def int4_dequant_exact(q, s7) -> np.ndarray:
+    """q * s7 exactly (fp64): the weight value the 4-bit path on the FP8 matrix core
+    stands for.  The codes -7..7 are exact e4m3 values and the product of a 3-bit integer
+    and an fp32 scale is exact in fp64, so no rounding enters here."""
+    q = np.asarray(q, dtype=np.int8)
+    G, N, K = q.shape
+    return (q.reshape(G, N, K // 128, 128).astype(np.float64)
+            * np.asarray(s7, np.float32).astype(np.float64)[:, :, :, None]).reshape(G, N, K)
+
+
 def int4_pack(q) -> np.ndarray:
     """Pack int4 codes [..., K] into bytes [..., K/2] (a storage layout of this library).
 

@@ -10,7 +10,7 @@ import math
 import numpy as np
 
 from .codecs import (bf16_round, dequant_fp8_act, dequant_fp8_weight, int4_dequant,
-                     quant_fp8_act)
+                     int4_dequant_exact, quant_fp8_act)
 
 
 # --------------------------------------------------------------------- routing
@@ -181,6 +181,14 @@ def grouped_gemm(A, B, offsets) -> np.ndarray:
     return C
 
 
+def grouped_gemm_w4a8(qA, sA, q, s7, offsets) -> np.ndarray:
+    """Grouped GEMM of 1x128 e4m3 activations with block-wise 4-bit weights: C[r, n] = sum
+    over K blocks kb of sA[r,kb] * s7[g,n,kb] * sum_{k in kb} e4m3(qA[r,k]) * q[g,n,k]
+    (the lecture's 4-bit weights, tqpw.cn sec. 3.1, promoted per 128-deep block as the
+    FP8 path, qidao123.com day 3) -- the product of the dequantised operands, in fp64."""
+    return grouped_gemm(dequant_fp8_act(qA, sA), int4_dequant_exact(q, s7), offsets)
+
+
 def grouped_gemm_fp8(qA, sA, qB, sB, offsets) -> np.ndarray:
     """FP8 grouped GEMM with fine-grained scales, evaluated exactly enough.
 
@@ -238,6 +246,9 @@ def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
                   requantised 1x128 before the down projection.
     mode "w4a16": experts = (c13, s13, c2, s2) int4 codes with 1x128 per-channel
                   scales; x is used as bf16 directly; h is rounded to fp32 then bf16.
+    mode "w4a8":  the same int4 codes and scales, the weights taken exactly as q * s7
+                  (the codes are exact e4m3 operands); x and h quantised 1x128 e4m3 as in
+                  mode "fp8".
     Routing: score (softmax + bias top-k) when ``w_router`` is given, else hash.
     ``tokens`` (optional) restricts the expert computation to those tokens (every
     routing decision is still made for the whole batch); y rows of other tokens
@@ -263,7 +274,7 @@ def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
     out.update(counts=counts, offsets=offsets, row_of_slot=ros, slot_of_row=sor)
 
     want = np.ones(T, dtype=bool) if tokens is None else np.isin(np.arange(T), tokens)
-    if mode == "fp8":
+    if mode in ("fp8", "w4a8"):
         qx, sx = quant_fp8_act(xf)
         xin = dequant_fp8_act(qx, sx)
         out["qx"], out["sx"] = qx, sx
@@ -287,6 +298,10 @@ def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
             q13, s13, q2, s2 = experts
             w13 = dequant_fp8_weight(q13[e:e + 1], s13[e:e + 1])[0]
             w2 = dequant_fp8_weight(q2[e:e + 1], s2[e:e + 1])[0]
+        elif mode == "w4a8":
+            c13, s13, c2, s2 = experts
+            w13 = int4_dequant_exact(c13[e:e + 1], s13[e:e + 1])[0]
+            w2 = int4_dequant_exact(c2[e:e + 1], s2[e:e + 1])[0]
         else:
             c13, s13, c2, s2 = experts
             w13 = int4_dequant(c13[e:e + 1], s13[e:e + 1])[0].astype(np.float64)
@@ -294,7 +309,7 @@ def layer_forward(mode: str, x, *, E: int, k: int, I: int, m_align: int = 16,
         gu = a @ w13.T
         h = swiglu(gu[:, :I], gu[:, I:])
         h_exact = h
-        if mode == "fp8":
+        if mode in ("fp8", "w4a8"):
             qh, sh = quant_fp8_act(h.astype(np.float32))
             h = dequant_fp8_act(qh, sh)
         elif mode == "w4a16":

@@ -35,7 +35,8 @@ class Workload:
 
     mode: "fp32" (no quantisation), "fp8" (e4m3, 1x128 activation and
     128x128 weight block scales), "w4a16" (int4 1x128 per-channel weight
-    blocks, bf16 activations, hash routing).
+    blocks, bf16 activations), "w4a8" (the same int4 weights with 1x128 e4m3
+    activations).
     """
     name: str
     T: int
@@ -68,6 +69,9 @@ WORKLOADS = {
     # hash-routed layer with int4 expert weights
     "hash_w4a16": Workload("hash_w4a16", T=8192, d=4096, E=64, k=1, I=2048, mode="w4a16",
                            route="hash", m_align=128),
+    # the same layer with the 4-bit weights on the FP8 matrix core (1x128 e4m3 activations)
+    "hash_w4a8": Workload("hash_w4a8", T=8192, d=4096, E=64, k=1, I=2048, mode="w4a8",
+                          route="hash", m_align=128),
 }
 
 

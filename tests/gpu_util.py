@@ -176,19 +176,26 @@ def fp8_layer_errors(y_gpu, ref, tokens, T, k, h_gpu):
     }
 
 
-def staged_fp8_layer(M, T, E, k, I, m_align, x, weights, renorm=False, capacity=0):
-    """The fp8 layer forward through the individual C entry points on the current
-    stream (route -> dispatch -> quant -> GEMM1 -> GEMM2 -> combine).  The same kernels
-    on the same inputs as moe_layer_fwd, so the outputs agree bit for bit; returns every
-    intermediate, including GEMM1's requantised h (codes, scales) per expert row."""
+def staged_fp8_layer(M, T, E, k, I, m_align, x, weights, renorm=False, capacity=0,
+                     w4a8=False, token_ids=None):
+    """The fp8 (or 4-bit-weight W4A8) layer forward through the individual C entry points
+    on the current stream (route -> dispatch -> quant -> GEMM1 -> GEMM2 -> combine).  The
+    same kernels on the same inputs as moe_layer_fwd, so the outputs agree bit for bit;
+    returns every intermediate, including GEMM1's requantised h (codes, scales) per
+    expert row.  Hash routing when ``token_ids`` is given."""
     R = M.moe_rows_bound(T, k, E, m_align)
     d = x.shape[1]
-    idx, gw, logits = M.moe_route(x, weights["w_router"], weights["bias"], k, renorm)
+    if token_ids is not None:
+        idx, gw = M.moe_route_hash(token_ids, E)
+        logits = None
+    else:
+        idx, gw, logits = M.moe_route(x, weights["w_router"], weights["bias"], k, renorm)
     counts, offsets, ros, sor = M.moe_dispatch(idx, E, m_align, capacity)
     qx, sx = M.moe_quant_fp8(x)
-    hq, sh = M.grouped_gemm_fp8(qx, sx, weights["w13"], weights["s13"], offsets, R, I,
-                                swiglu=True, a_rows=sor, a_row_div=k)
-    o = M.grouped_gemm_fp8(hq, sh, weights["w2"], weights["s2"], offsets, R, d)
+    gemm = M.grouped_gemm_w4a8 if w4a8 else M.grouped_gemm_fp8
+    hq, sh = gemm(qx, sx, weights["w13"], weights["s13"], offsets, R, I, swiglu=True,
+                  a_rows=sor, a_row_div=k)
+    o = gemm(hq, sh, weights["w2"], weights["s2"], offsets, R, d)
     y = M.moe_combine(o, ros, gw, T, k)
     return {"y": y, "counts": counts, "offsets": offsets, "idx": idx, "w": gw,
             "logits": logits, "row_of_slot": ros, "slot_of_row": sor, "hq": hq, "sh": sh}

@@ -23,7 +23,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = _lib.load()
     declared = _declared()
-    assert len(declared) == 25, declared
+    assert len(declared) == 27, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -225,3 +225,14 @@ def test_chunked_pipeline_checks():
                                    None), "dropless")
     _err(lib.moe_layer_fwd_chunked(C.byref(d), C.byref(w), FAKE, None, FAKE, FAKE, n, 0, S, None),
          "chunk_tokens")
+
+
+def test_build_rejects_kernels_with_scratch():
+    """The build's spill check reads the compiler's resource remarks: a kernel with private
+    (scratch) memory is named, kernels without are not."""
+    from fp8_grouped_gemm_amd.build import scratch_users
+    remarks = """x.hip:1:1: remark: Function Name: _Zgood [-Rpass-analysis=kernel-resource-usage]
+x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+x.hip:9:1: remark: Function Name: _Zbad [-Rpass-analysis=kernel-resource-usage]
+x.hip:9:1: remark:     ScratchSize [bytes/lane]: 44 [-Rpass-analysis=kernel-resource-usage]"""
+    assert scratch_users(remarks) == ["_Zbad (44 bytes/lane)"]

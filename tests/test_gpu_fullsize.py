@@ -99,6 +99,9 @@ def _layer_fullsize(w: synth.Workload, tokens=None, n_tokens=16, max_experts=40,
         q2, s2 = M.moe_quant_weight_int4(inp["w2"])
     if w.mode == "fp8":
         q13, q2 = M.moe_pack_weight_fp8(q13), M.moe_pack_weight_fp8(q2)
+    elif w.mode == "w4a8":
+        q13, s13 = M.moe_pack_weight_int4(q13, s13)
+        q2, s2 = M.moe_pack_weight_int4(q2, s2)
     weights = {"w13": q13, "s13": s13, "w2": q2, "s2": s2}
     if w.route == "score":
         weights.update(w_router=inp["w_router"], bias=inp["bias"])
@@ -106,10 +109,11 @@ def _layer_fullsize(w: synth.Workload, tokens=None, n_tokens=16, max_experts=40,
                        capacity_factor=cap_factor, layout=layout)
     y, counts = M.moe_layer_fwd(desc, weights, inp["x"], inp.get("token_ids"))
     staged = None
-    if w.mode == "fp8":
+    if w.mode in ("fp8", "w4a8"):
         note(f"full-size layer {w.name}: the same steps through the individual entry points")
         staged = staged_fp8_layer(M, w.T, w.E, w.k, w.I, w.m_align, inp["x"], weights,
-                                  capacity=M.moe_capacity(w.T, w.k, w.E, cap_factor))
+                                  capacity=M.moe_capacity(w.T, w.k, w.E, cap_factor),
+                                  w4a8=w.mode == "w4a8", token_ids=inp.get("token_ids"))
         assert torch.equal(staged["y"], y) and torch.equal(staged["counts"], counts)
     torch.cuda.synchronize()
     del q13, q2
@@ -145,7 +149,7 @@ def _layer_fullsize(w: synth.Workload, tokens=None, n_tokens=16, max_experts=40,
                           w_router=None if ids is not None else inp["w_router"].float().cpu().numpy(),
                           bias=None if ids is not None else inp["bias"].cpu().numpy(),
                           token_ids=None if ids is None else ids.cpu().numpy(),
-                          experts=experts, tokens=tokens, keep=(w.mode == "fp8"),
+                          experts=experts, tokens=tokens, keep=(w.mode in ("fp8", "w4a8")),
                           cap_factor=cap_factor)
     if w.route == "score":
         free = ~near
@@ -155,7 +159,7 @@ def _layer_fullsize(w: synth.Workload, tokens=None, n_tokens=16, max_experts=40,
     else:
         np.testing.assert_array_equal(cnt, ref["counts"])
     yg = to_np(y[tokens]).astype(np.float64)
-    if w.mode == "fp8":
+    if w.mode in ("fp8", "w4a8"):
         h_gpu = gpu_h_by_slot(staged, [t * w.k + j for t in tokens for j in range(w.k)])
         e = fp8_layer_errors(yg, ref, np.asarray(tokens), w.T, w.k, h_gpu)
         print(f"errors {e}")
@@ -188,6 +192,12 @@ def test_fullsize_decode_layer_masked():
 
 def test_fullsize_hash_w4a16_layer():
     _layer_fullsize(synth.WORKLOADS["hash_w4a16"], [0, 1, 4096, 8191])
+
+
+def test_fullsize_hash_w4a8_layer():
+    """The hash-routed 4-bit layer's shape (T=8192, d=4096, E=64, I=2048) with the weights
+    kept 4-bit on the FP8 matrix core and 1x128 e4m3 activations."""
+    _layer_fullsize(synth.WORKLOADS["hash_w4a8"], [0, 1, 77, 4096, 5000, 8191])
 
 
 def test_fullsize_grouped_gemm_fp8():

@@ -569,3 +569,114 @@ def test_device_supported():
     """The GPU these tests run on is a gfx950: the library accepts it."""
     note("device supported")
     assert M.moe_device_supported(0)
+
+
+# ------------------------------------------------ 4-bit weights on the FP8 core
+
+def _pack_int4_reference(q, s7):
+    """moe_pack_weight_int4's order written out with numpy: codes [G][N/16][KB][64][16 B]
+    with lane l of block (nb, kb) holding bytes 64 kb + 16 (l // 16) .. +16 of row
+    16 nb + l % 16; scales [G][N/16][KB][16]."""
+    G, N, K2 = q.shape
+    KB = K2 // 64
+    x = q.reshape(G, N // 16, 16, KB, 4, 16)        # g, nb, r, kb, c, byte
+    x = x.transpose(0, 1, 3, 4, 2, 5)               # g, nb, kb, c, r, byte (lane = 16 c + r)
+    sf = s7.reshape(G, N // 16, 16, KB).transpose(0, 1, 3, 2)
+    return np.ascontiguousarray(x).reshape(G, N, K2), np.ascontiguousarray(sf).reshape(G, N, KB)
+
+
+def test_pack_weight_int4_permutation():
+    note("pack weight int4")
+    w = synth.normal((3, 256, 384), 17, "w13", std=0.02)
+    q, s7 = M.moe_quant_weight_int4(w.to(dev()))
+    qf, s7f = M.moe_pack_weight_int4(q, s7)
+    rq, rs = _pack_int4_reference(to_np(q), to_np(s7))
+    np.testing.assert_array_equal(to_np(qf), rq)
+    np.testing.assert_array_equal(to_np(s7f), rs)
+
+
+def _w4a8_case(sizes, N, K, m_align, seed, swiglu):
+    a, b, offsets, R = _gemm_case(sizes, N, K, m_align, seed, swiglu)
+    qa, sa = M.moe_quant_fp8(a.to(dev()))
+    qb, s7 = M.moe_quant_weight_int4(b.to(dev()))
+    qbf, s7f = M.moe_pack_weight_int4(qb, s7)
+    qao, sao = OC.quant_fp8_act(a.numpy())
+    cbo, s7o = OC.int4_quant_rows(b.numpy())
+    np.testing.assert_array_equal(to_np(qb), OC.int4_pack(cbo))
+    np.testing.assert_array_equal(to_np(s7), s7o)
+    live = np.zeros(R, bool)
+    for g in range(len(sizes)):
+        live[offsets[g]:offsets[g] + sizes[g]] = True
+    return qa, sa, qbf, s7f, qao, sao, cbo, s7o, offsets, R, live
+
+
+@pytest.mark.parametrize("sizes,m_align,K", [
+    ([128, 256, 64, 512, 128, 256, 64, 512], 128, 512),   # 128-row tiles
+    ([0, 1, 17, 130, 300, 0], 16, 384),                     # empty, tiny, ragged groups
+    ([5, 3, 9, 2, 7, 1, 4, 6, 8, 3], 8, 256),              # decode-sized groups (16-row tiles)
+    ([40, 33, 50, 20], 32, 1536),                          # 32-row tiles, longer K
+    ([3, 20, 40, 150], 16, 128),                           # one K block
+])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_w4a8(sizes, m_align, K, swiglu):
+    """4-bit weights (every code -7..7 occurs) expanded to e4m3 in registers on the FP8
+    matrix core, promoted per block with the row scale and each channel's own scale."""
+    N = 128 if swiglu else 256
+    note(f"gemm w4a8 sizes={sizes} m_align={m_align} K={K} swiglu={swiglu}")
+    qa, sa, qbf, s7f, qao, sao, cbo, s7o, offsets, R, live = _w4a8_case(sizes, N, K, m_align,
+                                                                        61, swiglu)
+    assert set(np.unique(cbo).tolist()) == set(range(-7, 8))
+    off_d = torch.from_numpy(offsets).to(dev())
+    ref = O.grouped_gemm_w4a8(qao, sao, cbo, s7o, offsets)
+    if not swiglu:
+        c = M.grouped_gemm_w4a8(qa, sa, qbf, s7f, off_d, R, N)
+        beyond, raw = error_ratios(to_np(c)[live], ref[live])
+        print(f"beyond={beyond:.3e} raw={raw:.3e}")
+        assert beyond <= TOL, beyond
+    else:
+        codes, sc = M.grouped_gemm_w4a8(qa, sa, qbf, s7f, off_d, R, N, swiglu=True)
+        A = OC.dequant_fp8_act(qao, sao)
+        Bd = OC.int4_dequant_exact(cbo, s7o)
+        sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)
+        _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
+
+
+def test_grouped_gemm_w4a8_gather():
+    """GEMM1's activation gather with 4-bit weights: logical row r reads token a_rows[r] // k."""
+    note("gemm w4a8 gather")
+    T, k, E, N, K = 50, 2, 4, 128, 256
+    idx = synth.random_topk(T, E, k, seed=4)
+    counts, offsets, ros, sor = O.dispatch(idx, E, 16)
+    x = synth.normal((T, K), 12, "x", dtype=torch.bfloat16)
+    w = synth.normal((E, N, K), 12, "w13", std=K ** -0.5)
+    qx, sx = M.moe_quant_fp8(x.to(dev()))
+    qw, s7 = M.moe_quant_weight_int4(w.to(dev()))
+    qwf, s7f = M.moe_pack_weight_int4(qw, s7)
+    R = len(sor)
+    c = M.grouped_gemm_w4a8(qx, sx, qwf, s7f, torch.from_numpy(offsets).to(dev()), R, N,
+                            a_rows=torch.from_numpy(sor).to(dev()), a_row_div=k)
+    qxo, sxo = OC.quant_fp8_act(x.float().numpy())
+    cwo, s7o = OC.int4_quant_rows(w.numpy())
+    live = sor >= 0
+    A = np.zeros((R, K), np.uint8)
+    sA = np.ones((R, K // 128), np.float32)
+    A[live] = qxo[sor[live] // k]
+    sA[live] = sxo[sor[live] // k]
+    ref = O.grouped_gemm_w4a8(A, sA, cwo, s7o, offsets)
+    beyond, raw = error_ratios(to_np(c)[live], ref[live])
+    assert beyond <= TOL
+
+
+@pytest.mark.parametrize("sizes,K", [([3, 20, 40, 150], 128), ([128, 256, 64, 512], 512)])
+def test_determinism_w4a8(sizes, K):
+    """Repeated 4-bit-weight SwiGLU launches give identical codes and scales (a regression
+    test for the copy order the kernel's counted waits rely on: the first block's
+    activation copy must be issued before the weight loads the prologue replays)."""
+    note(f"determinism w4a8 sizes={sizes} K={K}")
+    qa, sa, qbf, s7f, *_, offsets, R, live = _w4a8_case(sizes, 128, K, 16, 71, True)
+    off = torch.from_numpy(offsets).to(dev())
+    runs = [M.grouped_gemm_w4a8(qa, sa, qbf, s7f, off, R, 128, swiglu=True) for _ in range(6)]
+    torch.cuda.synchronize()
+    for c, s in runs[1:]:
+        assert np.array_equal(to_np(c)[live], to_np(runs[0][0])[live])
+        assert np.array_equal(to_np(s)[live], to_np(runs[0][1])[live])

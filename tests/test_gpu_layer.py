@@ -20,6 +20,11 @@ def _gpu_weights(w: synth.Workload, inp: dict) -> dict:
     out = {k: (v.to(d) if v is not None else None) for k, v in out.items()}
     if w.mode == "fp32":
         out["w13"], out["w2"] = inp["w13"].to(d), inp["w2"].to(d)
+    elif w.mode == "w4a8":
+        q13, s13 = M.moe_quant_weight_int4(inp["w13"].to(d))
+        q2, s2 = M.moe_quant_weight_int4(inp["w2"].to(d))
+        out["w13"], out["s13"] = M.moe_pack_weight_int4(q13, s13)
+        out["w2"], out["s2"] = M.moe_pack_weight_int4(q2, s2)
     elif w.mode == "fp8":
         q13, out["s13"] = M.moe_quant_weight_fp8(inp["w13"].to(d))
         q2, out["s2"] = M.moe_quant_weight_fp8(inp["w2"].to(d))
@@ -34,6 +39,8 @@ def _oracle_experts(w: synth.Workload, inp: dict):
     w13, w2 = inp["w13"].cpu().numpy(), inp["w2"].cpu().numpy()
     if w.mode == "fp32":
         return (w13, w2)
+    if w.mode == "w4a8":
+        return (*OC.int4_quant_rows(w13), *OC.int4_quant_rows(w2))
     if w.mode == "fp8":
         return (*OC.quant_fp8_weight(w13), *OC.quant_fp8_weight(w2))
     return (*OC.int4_quant_rows(w13), *OC.int4_quant_rows(w2))
@@ -61,11 +68,13 @@ def run_layer_case(w: synth.Workload, tokens=None, cap_factor=0.0, renorm=False,
     ids = inp.get("token_ids")
     y, counts = M.moe_layer_fwd(desc, gw, x, ids.to(dev()) if ids is not None else None)
     staged = None
-    if w.mode == "fp8":
+    if w.mode in ("fp8", "w4a8"):
         # the same kernels through the individual entry points: bit-identical, and they
         # expose GEMM1's requantised h for the flip accounting below
         staged = staged_fp8_layer(M, w.T, w.E, w.k, w.I, w.m_align, x, gw, renorm=renorm,
-                                  capacity=M.moe_capacity(w.T, w.k, w.E, cap_factor))
+                                  capacity=M.moe_capacity(w.T, w.k, w.E, cap_factor),
+                                  w4a8=w.mode == "w4a8",
+                                  token_ids=ids.to(dev()) if ids is not None else None)
         # (masked layout: the same expert rows at other places, so the same y bit for bit)
         assert torch.equal(staged["y"], y) and torch.equal(staged["counts"], counts)
     torch.cuda.synchronize()
@@ -75,7 +84,8 @@ def run_layer_case(w: synth.Workload, tokens=None, cap_factor=0.0, renorm=False,
                           bias=None if w.route == "hash" else inp["bias"].numpy(),
                           token_ids=None if ids is None else ids.numpy(),
                           experts=_oracle_experts(w, inp), tokens=tokens,
-                          keep=(w.mode == "fp8"), cap_factor=cap_factor, renorm=renorm)
+                          keep=(w.mode in ("fp8", "w4a8")), cap_factor=cap_factor,
+                          renorm=renorm)
     rows = np.arange(w.T) if tokens is None else np.asarray(tokens)
     if w.route == "score":
         amb = _near_ties(ref["logits"].astype(np.float32), inp["bias"].numpy(), w.k, 1e-5)
@@ -94,7 +104,7 @@ def run_layer_case(w: synth.Workload, tokens=None, cap_factor=0.0, renorm=False,
         print(f"raw={raw:.3e}")
         assert raw <= TOL
         return ref
-    if w.mode == "fp8":
+    if w.mode in ("fp8", "w4a8"):
         slots = [t * w.k + j for t in keep for j in range(w.k)]
         np.testing.assert_array_equal(to_np(staged["idx"])[keep], ref["idx"][keep])
         h_gpu = gpu_h_by_slot(staged, slots)
@@ -159,6 +169,17 @@ def test_layer_masked_layout(cap_factor):
     w = synth.Workload("masked_fp8", T=96, d=256, E=8, k=2, I=256, mode="fp8",
                        skew_frac=0.25, skew_add=2.0, m_align=16, seed=5)
     run_layer_case(w, cap_factor=cap_factor, layout="masked")
+
+
+def test_layer_small_w4a8():
+    """4-bit expert weights on the FP8 matrix core, score routing."""
+    run_layer_case(synth.Workload("small_w4a8", T=96, d=256, E=8, k=2, I=256, mode="w4a8",
+                                  skew_frac=0.25, skew_add=2.0, m_align=16, seed=2))
+
+
+def test_layer_small_w4a8_hash():
+    run_layer_case(synth.Workload("small_w4a8_hash", T=300, d=256, E=8, k=1, I=256,
+                                  mode="w4a8", route="hash", m_align=64))
 
 
 def test_layer_small_w4a16_hash():

@@ -211,3 +211,32 @@ def test_int4_quant_dequant_roundtrip_exact_codes():
     np.testing.assert_array_equal(q, q0)
     assert np.all(s7o == s7)
     np.testing.assert_array_equal(C.int4_dequant(q, s7o), w)
+
+
+def test_int4_codes_exact_as_e4m3_every_code():
+    """Each of the 15 codes -7..7 the lecture's 4-bit rule produces (tqpw.cn sec. 3.1) is an
+    exact e4m3 value: encoding and decoding returns the integer, so the FP8 matrix core
+    multiplies them exactly.  Also their e4m3 bit patterns, from the format's definition
+    (sign, exponent with bias 7, 3 mantissa bits)."""
+    q = np.arange(-7, 8, dtype=np.float64)
+    codes = C.e4m3_encode(q)
+    np.testing.assert_array_equal(C.e4m3_decode(codes), q)
+    # 1 = 1.0 x 2^0 -> exponent field 7; 3 = 1.5 x 2^1; 5 = 1.25 x 2^2; 7 = 1.75 x 2^2
+    want = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 5: 0x4A, 6: 0x4C, 7: 0x4E}
+    for v, c in zip(q.astype(int), codes):
+        assert int(c) == (want[abs(v)] | (0x80 if v < 0 else 0)), (v, hex(c))
+
+
+def test_int4_dequant_exact_relations():
+    """The exact 4-bit weight q * s7 against brute-force products of Python floats (exact:
+    3-bit integers times fp32 values fit an fp64 mantissa), and the W4A16 weight is its
+    fp32 rounding rounded to bf16."""
+    rng = np.random.default_rng(31)
+    q = rng.integers(-7, 8, (2, 3, 256)).astype(np.int8)
+    s7 = (rng.uniform(0.5, 2.0, (2, 3, 2)) * 2.0 ** rng.integers(-12, 3, (2, 3, 2))).astype(np.float32)
+    ex = C.int4_dequant_exact(q, s7)
+    for g in range(2):
+        for n in range(3):
+            for k in range(256):
+                assert ex[g, n, k] == int(q[g, n, k]) * float(s7[g, n, k // 128])
+    np.testing.assert_array_equal(C.bf16_round(ex.astype(np.float32)), C.int4_dequant(q, s7))

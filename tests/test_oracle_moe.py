@@ -414,3 +414,65 @@ def test_layer_output_is_combine_of_expert_rows():
         o_rows[ros[s]] = v
     np.testing.assert_allclose(out["y"], O.combine(o_rows, ros, out["w"], T, k),
                                rtol=1e-14, atol=1e-14)
+
+
+def test_grouped_gemm_w4a8_exact_fractions():
+    """The 4-bit-weight grouped GEMM against exact rational arithmetic on random codes
+    (every code -7..7) and scales: C = sum_kb sA * s7 * sum_k e4m3(qA) * q."""
+    rng = np.random.default_rng(13)
+    G, N, K = 2, 3, 256
+    offsets = np.array([0, 2, 5])
+    qA = rng.integers(0, 256, (5, K)).astype(np.uint8)
+    qA[(qA & 0x7F) == 0x7F] = 0x11                     # no NaN codes
+    sA = rng.uniform(0.01, 2, (5, K // 128)).astype(np.float32)
+    q = rng.integers(-7, 8, (G, N, K)).astype(np.int8)
+    s7 = rng.uniform(0.001, 0.1, (G, N, K // 128)).astype(np.float32)
+    got = O.grouped_gemm_w4a8(qA, sA, q, s7, offsets)
+    dec = C.e4m3_decode_table()
+    for g in range(G):
+        for r in range(offsets[g], offsets[g + 1]):
+            for n in range(N):
+                tot = Fraction(0)
+                for kb in range(K // 128):
+                    part = sum(Fraction(float(dec[qA[r, k]])) * int(q[g, n, k])
+                               for k in range(kb * 128, kb * 128 + 128))
+                    tot += Fraction(float(sA[r, kb])) * Fraction(float(s7[g, n, kb])) * part
+                assert math.isclose(got[r, n], float(tot), rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_layer_w4a8_matches_restatement():
+    """The 4-bit-weight layer on the FP8 path equals the same maths written with torch: the
+    weights q * s7, the activations and h through torch's own e4m3 cast at 1x128 scales."""
+    T, d, E, k, I = 16, 256, 4, 2, 128
+    x = synth.normal((T, d), 6, "x", dtype=torch.bfloat16).float().numpy()
+    wr = synth.normal((E, d), 6, "w_gate_router", std=d ** -0.5,
+                      dtype=torch.bfloat16).float().numpy()
+    b = synth.uniform((E,), -0.01, 0.01, 6, "bias").numpy()
+    w13, w2 = _fp32_experts(E, d, I, 6)
+    c13, s13 = C.int4_quant_rows(w13)
+    c2, s2 = C.int4_quant_rows(w2)
+    out = O.layer_forward("w4a8", x, E=E, k=k, I=I, w_router=wr, bias=b,
+                          experts=(c13, s13, c2, s2))
+
+    def q1x128(v):
+        vb = v.view(v.shape[0], -1, 128)
+        s = vb.abs().amax(dim=2) / 448.0
+        s = torch.where(s == 0, torch.ones_like(s), s)
+        qv = (vb / s[:, :, None]).clamp(-448, 448).to(torch.float8_e4m3fn).double()
+        return (qv * s.double()[:, :, None]).view(v.shape)
+
+    def w_exact(c, s7):
+        ct = torch.from_numpy(c.astype(np.float64))
+        return ct * torch.from_numpy(s7.astype(np.float64)).repeat_interleave(128, dim=-1)
+
+    xd = q1x128(torch.from_numpy(x))
+    W13, W2 = w_exact(c13, s13), w_exact(c2, s2)
+    y = torch.zeros(T, d, dtype=torch.float64)
+    for t in range(T):
+        for j in range(k):
+            e = int(out["idx"][t, j])
+            gu = W13[e] @ xd[t]
+            h = (torch.nn.functional.silu(gu[:I]) * gu[I:]).float()
+            hd = q1x128(h[None])[0]
+            y[t] += out["w"][t, j] * (W2[e] @ hd)
+    np.testing.assert_allclose(out["y"], y.numpy(), rtol=1e-12, atol=1e-12)
