@@ -407,15 +407,27 @@ def main(argv=None):
     return 0
 
 
+GEMM_SOURCES = ("gemm_fp8.hip", "gemm_fp8_kernel.hpp", "gemm_fp8_big.hip", "tiles.hpp",
+                "dma.hpp", "common.hpp")
+
+
+def gemm_source_sha256():
+    """One digest over every source the FP8 GEMM kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(ROOT, "fp8_grouped_gemm_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of a GEMM kernel from the committed rocprofv3 counter summary,
     or None when the kernel source changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "gemm_fp8_prefill_traffic.json")
-    src = os.path.join(ROOT, "fp8_grouped_gemm_amd", "csrc", "gemm_fp8.hip")
     try:
         d = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = gemm_source_sha256()
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_sha256") != sha:

@@ -36,6 +36,7 @@ FILE_FLAGS = {
     # accvgpr moves
     "gemm_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gemm_w4a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm_fp8_big.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

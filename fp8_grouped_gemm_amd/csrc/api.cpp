@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/moe.h"
@@ -77,6 +78,18 @@ inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 // The layer applies the same rule to its own rows bound, so the layer and the entry
 // point pick the same kernel for the same problem.
 int pick_bm(double rows_per_group) { return rows_per_group <= 32 ? 16 : 32; }
+
+// 256 x 256 tiles (a second kernel, launched first) for the whole 256-row tiles of the
+// groups that hold them, where the groups average at least 256 rows and K spans an even
+// number of 128-deep blocks.  Opt-in: FP8GG_BIG_TILES=1 in the environment (read at each
+// call) turns them on; measured on MI355X they are still slower than the 128-row tiles
+// alone (dense 8192 x 4096 x 7168: 1.79 vs 1.96 PFLOP/s).  The result meets the same error
+// bound either way (bit-identical in the measured cases).
+bool want_big(double rows_per_group, int K) {
+  const char* e = std::getenv("FP8GG_BIG_TILES");
+  if (!e || e[0] != '1') return false;
+  return rows_per_group >= 256 && (K / 128) % 2 == 0;
+}
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -350,7 +363,8 @@ int grouped_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows, i
   if ((st = current_device(&cus))) return st;
   const int bm = pick_bm((double)R_cap / G);
   return hip_status(moe::launch_gemm_fp8(A, sA, a_rows, a_row_div, B, sB, offsets, G, R_cap, N, K,
-                                         swiglu, C, sC, bm, cus, S(stream)),
+                                         swiglu, C, sC, bm, cus, S(stream), moe::kRowsOffsets, 0,
+                                         want_big((double)R_cap / G, K)),
                     "grouped_gemm_fp8 launch");
 }
 
@@ -384,7 +398,7 @@ int grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B,
   if ((st = current_device(&cus))) return st;
   return hip_status(moe::launch_gemm_fp8(A, sA, nullptr, 1, B, sB, counts, G, rows, N, K, swiglu,
                                          C, sC, pick_bm(cap), cus, S(stream),
-                                         moe::kRowsMasked, cap),
+                                         moe::kRowsMasked, cap, want_big(cap, K)),
                     "grouped_gemm_fp8_masked launch");
 }
 
@@ -448,7 +462,7 @@ int gemm_fp8(const uint8_t* A, const float* sA, const uint8_t* B, const float* s
   if (st) return st;
   return hip_status(moe::launch_gemm_fp8(A, sA, nullptr, 1, B, sB, nullptr, 1, M, N, K, false, C,
                                          nullptr, pick_bm(M), cus, S(stream),
-                                         moe::kRowsDense, M),
+                                         moe::kRowsDense, M, want_big(M, K)),
                     "gemm_fp8 launch");
 }
 
@@ -689,20 +703,21 @@ int layer_back(const moe_layer_desc* d, const moe_layer_weights* w, const void* 
     const int cap = R / E;
     STEP(moe::launch_gemm_fp8(P.qx, P.sx, nullptr, 1, static_cast<const uint8_t*>(w->w13),
                               w->s13, P.counts, E, R, I, D, true, P.hq, P.sh, pick_bm(cap), cus,
-                              s, moe::kRowsMasked, cap),
+                              s, moe::kRowsMasked, cap, want_big(cap, D)),
          "masked gemm1 launch");
     STEP(moe::launch_gemm_fp8(P.hq, P.sh, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
                               P.counts, E, R, D, I, false, P.o, nullptr, pick_bm(cap), cus, s,
-                              moe::kRowsMasked, cap),
+                              moe::kRowsMasked, cap, want_big(cap, I)),
          "masked gemm2 launch");
   } else if (d->mode == MOE_MODE_FP8) {
     STEP(moe::launch_gemm_fp8(P.qx, P.sx, P.sor, k, static_cast<const uint8_t*>(w->w13), w->s13,
                               P.offsets, E, R, I, D, true, P.hq, P.sh, pick_bm(rows_per_group),
-                              cus, s),
+                              cus, s, moe::kRowsOffsets, 0, want_big(rows_per_group, D)),
          "gemm1 launch");
     STEP(moe::launch_gemm_fp8(P.hq, P.sh, nullptr, 1, static_cast<const uint8_t*>(w->w2), w->s2,
                               P.offsets, E, R, D, I, false, P.o, nullptr,
-                              pick_bm(rows_per_group), cus, s),
+                              pick_bm(rows_per_group), cus, s, moe::kRowsOffsets, 0,
+                              want_big(rows_per_group, I)),
          "gemm2 launch");
   } else if (d->mode == MOE_MODE_W4A8) {
     STEP(moe::launch_gemm_w4a8(P.qx, P.sx, P.sor, k, static_cast<const uint8_t*>(w->w13), w->s13,

@@ -15,12 +15,13 @@ namespace moe {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// (An LDS DMA needs one wait state after the write of M0 that addresses it.)
 __device__ __forceinline__ void dma16(const void* g, uint32_t m) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(m), "v"(g) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t m) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :: "s"(m), "v"(g) : "memory", "m0");
 }
 

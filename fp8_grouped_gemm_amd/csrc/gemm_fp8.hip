@@ -44,9 +44,19 @@ hipError_t launch_pack_weight_fp8(const uint8_t* B, int G, int R, int K, uint8_t
 hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows, int a_row_div,
                            const uint8_t* Bf, const float* sB, const int32_t* offsets, int G,
                            int R_cap, int N, int K, bool swiglu, void* C, float* sC, int bm,
-                           int num_cus, hipStream_t s, int rows_mode, int cap) {
+                           int num_cus, hipStream_t s, int rows_mode, int cap, bool big) {
+  // 256-column tiles (SwiGLU: 128 output columns from 256 weight rows), an even number of
+  // K blocks, and a group's weights within 32-bit offsets
+  big = big && (swiglu || N % 256 == 0) && (K / 128) % 2 == 0 &&
+        (long long)(swiglu ? 2 * N : N) * K < (1LL << 31);
+  if (big) {
+    const hipError_t e = launch_gemm_fp8_big(A, sA, a_rows, a_row_div, Bf, sB, offsets, G, N, K,
+                                             swiglu, C, sC, num_cus, s, rows_mode, cap);
+    if (e != hipSuccess) return e;
+  }
   return launch_gemm_impl<false>(A, sA, a_rows, a_row_div, Bf, sB, offsets, G, R_cap, N, K,
-                                 swiglu, C, sC, bm, num_cus, s, rows_mode, cap);
+                                 swiglu, C, sC, bm, num_cus, s, rows_mode, cap,
+                                 big ? big_rows_per_round(N, swiglu, num_cus) : -1);
 }
 
 }  // namespace moe

@@ -72,6 +72,9 @@ struct GemmArgs {
   // compiler fence that keeps every block's count of vector memory operations in
   // order, which the counted waits for the activation copies rely on.
   const float* wsc;
+  // >= 0: a 256-row-tile launch with that many row tiles per round handles the leading
+  // whole 256-row tiles (big_cut); this launch takes the rest of every group
+  int big_rpr;
 };
 
 // wait for this wave's LDS operations, then for the whole workgroup
@@ -164,7 +167,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     return (k & 1) | ((k & 2) << 1);
   };
 
-  build_tile_map<BMS, BMB, NT, true>(tm, args.offsets, G, args.mode, args.cap);
+  __shared__ int skip_s[kMaxGroups + 1];
+  build_tile_map<BMS, BMB, NT, true>(tm, args.offsets, G, args.mode, args.cap, args.big_rpr,
+                                     skip_s);
   // large-group (128-row, MFMA-bound) and small-group (weight-streaming) tile lists
   const int n_big = tm.start[G] * tiles_n, n_small = tm.sstart[G] * tiles_n;
   const int P = gridDim.x, b = blockIdx.x;
@@ -720,8 +725,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     const int mi = sr * GM + idx % rows_sr, ni = idx / rows_sr;
     // tile coordinates are the same in every lane: scalar registers
     const int gu = __builtin_amdgcn_readfirstlane(g);
-    const int rows = __builtin_amdgcn_readfirstlane(group_rows(tm, gu));
-    const int r0 = __builtin_amdgcn_readfirstlane(group_row0(tm, gu));
+    const int* skip = args.big_rpr >= 0 ? skip_s : nullptr;
+    const int rows = __builtin_amdgcn_readfirstlane(group_rows(tm, gu, skip));
+    const int r0 = __builtin_amdgcn_readfirstlane(group_row0(tm, gu, skip));
     const int n0 = __builtin_amdgcn_readfirstlane(ni * BN_OUT);
     const int miu = __builtin_amdgcn_readfirstlane(mi);
     // small tiles stream weights and gain nothing from the product tables (their
@@ -744,10 +750,10 @@ hipError_t launch_gemm_impl(const uint8_t* A, const float* sA, const int32_t* a_
                             int a_row_div, const uint8_t* Bf, const float* sB,
                             const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
                             void* C, float* sC, int bm, int num_cus, hipStream_t s,
-                            int rows_mode, int cap) {
+                            int rows_mode, int cap, int big_rpr = -1) {
   if (K / 128 > kGemmMaxKBlocks) return hipErrorInvalidValue;
   GemmArgs a{A, sA, a_rows, a_row_div, Bf, offsets, G, N, K, C, sC, rows_mode, cap,
-             W4 ? sB : nullptr};
+             W4 ? sB : nullptr, big_rpr};
   const long tiles_n = swiglu ? N / 128 : (N + 255) / 256;
   const long mtiles = R_cap / (bm < 128 ? bm : 64) + G;
   long grid = std::min<long>(mtiles * tiles_n, (long)num_cus);

@@ -38,11 +38,20 @@ hipError_t launch_pack_weight_fp8(const uint8_t* B, int G, int R, int K, uint8_t
                                   hipStream_t s);
 // bm: rows per tile of small groups (16, 32, 64; larger values mean 64); Bf is
 // fragment-major (launch_pack_weight_fp8)
+// big: the whole 256-row tiles of large groups, in whole rounds of the grid, go to a
+// 256 x 256-tile kernel launched first (N a multiple of 256, or SwiGLU); the rest of every
+// group to the 128-row / small-tile kernel after it
 hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_rows,
                            int a_row_div, const uint8_t* B, const float* sB,
                            const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
                            void* C, float* sC, int bm, int num_cus, hipStream_t s,
-                           int rows_mode = 0, int cap = 0);
+                           int rows_mode = 0, int cap = 0, bool big = false);
+// the 256 x 256-tile kernel alone, and its row tiles per round (the cut both launches use)
+int big_rows_per_round(int N, bool swiglu, int num_cus);
+hipError_t launch_gemm_fp8_big(const uint8_t* A, const float* sA, const int32_t* a_rows,
+                               int a_row_div, const uint8_t* Bf, const float* sB,
+                               const int32_t* offsets, int G, int N, int K, bool swiglu, void* C,
+                               float* sC, int num_cus, hipStream_t s, int rows_mode, int cap);
 // int4 codes [G][R][K/2] and scales [G][R][K/128] -> the fragment-major order the W4A8
 // GEMM loads: codes [G][R/16][K/128][64][16 B], scales [G][R/16][K/128][16]
 hipError_t launch_pack_weight_int4(const uint8_t* q, const float* s7, int G, int R, int K,

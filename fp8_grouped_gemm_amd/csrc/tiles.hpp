@@ -26,24 +26,76 @@ struct TileMap {
   int mode, cap;              // GroupRows and C (masked) or M (dense)
 };
 
-// first row and row count of group g
-__device__ __forceinline__ int group_row0(const TileMap& tm, int g) {
+// first row and row count of group g, before any rows are handed to a 256-row-tile launch
+__device__ __forceinline__ int group_row0_all(const TileMap& tm, int g) {
   return tm.mode == kRowsMasked ? g * tm.cap : tm.off[g];
 }
-__device__ __forceinline__ int group_rows(const TileMap& tm, int g) {
+__device__ __forceinline__ int group_rows_all(const TileMap& tm, int g) {
   return tm.mode == kRowsMasked ? tm.off[g] : tm.off[g + 1] - tm.off[g];
+}
+// the rows this launch handles: skip (an LDS array, or null) holds each group's leading
+// rows that a 256-row-tile launch handles
+__device__ __forceinline__ int group_row0(const TileMap& tm, int g, const int* skip = nullptr) {
+  return group_row0_all(tm, g) + (skip ? skip[g] : 0);
+}
+__device__ __forceinline__ int group_rows(const TileMap& tm, int g, const int* skip = nullptr) {
+  return group_rows_all(tm, g) - (skip ? skip[g] : 0);
+}
+
+// Exclusive prefix over groups of count(g) into pre[0..G] (pre[G] = the total), by the
+// NT threads of the workgroup; every thread must call it.
+template <int NT, typename F>
+__device__ void group_prefix(int* pre, int G, F count) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ int ws[NW];
+  const int per = (G + NT - 1) / NT;
+  const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
+  int local = 0;
+  for (int g = g0; g < g1; ++g) local += count(g);
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) ws[wid] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += ws[w];
+  int run = base + incl - local;
+  for (int g = g0; g < g1; ++g) {
+    pre[g] = run;
+    run += count(g);
+  }
+  if (tid == NT - 1) pre[G] = base + incl;
+  __syncthreads();
+}
+
+// Rows of 256-row tiles: a group of M rows holds M / 256 whole ones.  A launch of those
+// tiles takes whole rounds of its grid: the first cut row tiles in group order, cut =
+// total rounded down to a multiple of rpr (row tiles per round; rpr = 0: all of them).
+constexpr int kBigRows = 256;
+__device__ __forceinline__ int big_cut(int total, int rpr) {
+  return rpr > 0 ? total / rpr * rpr : total;
 }
 
 // Rows per tile of a group with M rows: BMS for small groups (M <= BMS), BMB otherwise.
 template <int BMS, int BMB>
 __device__ __forceinline__ int tile_rows(int M) { return M <= BMS ? BMS : BMB; }
 
+// big_rpr >= 0 (with an LDS array skip_buf of G + 1 ints): the leading whole 256-row
+// tiles that a 256-row-tile launch with that many row tiles per round takes (big_cut)
+// are skipped here.
 template <int BMS, int BMB = BMS, int NT = 256, bool SPLIT = false>
 __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int G,
-                               int mode = kRowsOffsets, int cap = 0) {
+                               int mode = kRowsOffsets, int cap = 0, int big_rpr = -1,
+                               int* skip_buf = nullptr) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   __shared__ int wsum[NW], wsum2[NW];
+  const bool split = big_rpr >= 0 && skip_buf;
+  const int* skip = split ? skip_buf : nullptr;
   if (tid == 0) {
     tm.mode = mode;
     tm.cap = cap;
@@ -54,13 +106,23 @@ __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets,
     else tm.off[i] = i == 0 ? 0 : cap;
   }
   __syncthreads();
+  if (split) {
+    // the 256-row-tile launch's prefix, kept in start until the tile counts replace it
+    group_prefix<NT>(tm.start, G, [&](int g) { return group_rows_all(tm, g) / kBigRows; });
+    const int cut = big_cut(tm.start[G], big_rpr);
+    for (int g = tid; g < G; g += NT) {
+      const int nb = group_rows_all(tm, g) / kBigRows;
+      skip_buf[g] = kBigRows * min(max(cut - tm.start[g], 0), nb);
+    }
+    __syncthreads();
+  }
   // each thread owns a contiguous chunk of groups
   const int per = (G + NT - 1) / NT;
   const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
   // row tiles of group g: all of them (combined map) or, for a split map, the large
   // groups' (first) and the small groups' (second)
   auto count = [&](int g, int& big, int& small) {
-    const int M = group_rows(tm, g);
+    const int M = group_rows(tm, g, skip);
     if (SPLIT) {
       big = M > BMS ? (M + BMB - 1) / BMB : 0;
       small = (M > 0 && M <= BMS) ? 1 : 0;

@@ -100,6 +100,21 @@ def requant_band(h, dh):
     return q, s, q_lo, q_hi, delta, rho
 
 
+def check_swiglu_codes(codes, sc, ref, sab, N):
+    """GPU SwiGLU+requant output against the oracle's h within the MFMA error model:
+    unambiguous codes bit-exact, the rest one of the two correct neighbours."""
+    from oracle import codecs as OC
+    h, dh = swiglu_error_model(ref[:, :N], ref[:, N:], sab[:, :N], sab[:, N:])
+    q, s, q_lo, q_hi, delta, rho = requant_band(h, dh)
+    assert np.all(np.abs(sc.astype(np.float64) - s) <= s * rho * 1.01)
+    dg = OC.e4m3_decode(codes)
+    ok = (dg >= np.minimum(OC.e4m3_decode(q_lo), OC.e4m3_decode(q_hi))) & \
+         (dg <= np.maximum(OC.e4m3_decode(q_lo), OC.e4m3_decode(q_hi)))
+    unique = q_lo == q_hi
+    np.testing.assert_array_equal(codes[unique], q[unique])
+    assert ok.all()
+
+
 def fp8_layer_errors(y_gpu, ref, tokens, T, k, h_gpu):
     """Error ratios of a GPU fp8 layer output against the oracle (``ref`` from
     layer_forward(..., keep=True)) on the rows ``tokens``.

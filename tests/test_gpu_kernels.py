@@ -12,8 +12,8 @@ import fp8_grouped_gemm_amd as M
 import oracle as O
 from oracle import codecs as OC
 import synth
-from gpu_util import (TOL, dev, error_ratios, note, requant_band, swiglu_error_model,
-                      to_np)
+from gpu_util import (TOL, check_swiglu_codes, dev, error_ratios, note, requant_band,
+                      swiglu_error_model, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -309,20 +309,6 @@ def test_grouped_gemm_fp8_row_gather():
     assert beyond <= TOL
 
 
-def _check_swiglu_codes(codes, sc, ref, sab, N):
-    """GPU SwiGLU+requant output against the oracle's h within the MFMA error model:
-    unambiguous codes bit-exact, the rest one of the two correct neighbours."""
-    h, dh = swiglu_error_model(ref[:, :N], ref[:, N:], sab[:, :N], sab[:, N:])
-    q, s, q_lo, q_hi, delta, rho = requant_band(h, dh)
-    assert np.all(np.abs(sc.astype(np.float64) - s) <= s * rho * 1.01)
-    dg = OC.e4m3_decode(codes)
-    ok = (dg >= np.minimum(OC.e4m3_decode(q_lo), OC.e4m3_decode(q_hi))) & \
-         (dg <= np.maximum(OC.e4m3_decode(q_lo), OC.e4m3_decode(q_hi)))
-    unique = q_lo == q_hi
-    np.testing.assert_array_equal(codes[unique], q[unique])
-    assert ok.all()
-
-
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_grouped_gemm_fp8_masked(swiglu):
     """Fixed-capacity layout: group g owns rows [g*cap, g*cap + min(counts[g], cap))."""
@@ -352,7 +338,7 @@ def test_grouped_gemm_fp8_masked(swiglu):
             assert beyond <= TOL, (g, beyond)
         else:
             sab = O.grouped_gemm(np.abs(A[rows]), np.abs(Bd[g:g + 1]), one)
-            _check_swiglu_codes(to_np(out[0])[rows], to_np(out[1])[rows], ref, sab, N)
+            check_swiglu_codes(to_np(out[0])[rows], to_np(out[1])[rows], ref, sab, N)
 
 
 @pytest.mark.parametrize("K", [128, 256, 384, 640, 1536])
@@ -386,7 +372,7 @@ def test_grouped_gemm_fp8_short_k(K, sizes, m_align, swiglu):
         A = OC.dequant_fp8_act(qao, sao)
         Bd = OC.dequant_fp8_weight(qbo, sbo)
         sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)
-        _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
+        check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
 
 
 @pytest.mark.parametrize("case", ["max_k", "max_groups"])
@@ -424,7 +410,7 @@ def test_grouped_gemm_fp8_limits(case):
             A = OC.dequant_fp8_act(qao, sao)
             Bd = OC.dequant_fp8_weight(qbo, sbo)
             sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)
-            _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
+            check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
 
 
 @pytest.mark.parametrize("K", [8192, 8320])
@@ -456,7 +442,7 @@ def test_grouped_gemm_fp8_scale_table_forms(K, swiglu):
         A = OC.dequant_fp8_act(qao, sao)
         Bd = OC.dequant_fp8_weight(qbo, sbo)
         sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)
-        _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
+        check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
 
 
 @pytest.mark.parametrize("Mrows,K", [(0, 512), (1, 512), (200, 512), (333, 512),
@@ -638,7 +624,7 @@ def test_grouped_gemm_w4a8(sizes, m_align, K, swiglu):
         A = OC.dequant_fp8_act(qao, sao)
         Bd = OC.int4_dequant_exact(cbo, s7o)
         sab = O.grouped_gemm(np.abs(A), np.abs(Bd), offsets)
-        _check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
+        check_swiglu_codes(to_np(codes)[live], to_np(sc)[live], ref[live], sab[live], N)
 
 
 def test_grouped_gemm_w4a8_gather():
