@@ -192,22 +192,30 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(BigArgs args,
     }
     const uint32_t b_voff = lane * 16;
     const uint32_t s_voff = (uint32_t)row_src[(wid & 3) * 64 + lane] * (uint32_t)KB * 4u;
-    auto dma = [&](auto S, int kb) {
+    // piece q (0-8) of the copies of block kb into stage S
+    auto dma_piece = [&](auto S, int kb, int q) {
       constexpr int st = decltype(S)::value % 2;
-      uint8_t* ah0 = st == 0 ? a0 : a1;
-      uint8_t* ah1 = ah0 + BG_HALF;
-      const uint32_t ka = (uint32_t)kb * 128u, kbw = (uint32_t)kb * 2048u;
-      big_dma<16>(rs_a, a_voff[0], ka, ah0 + wid * 1024);
-      big_dma<16>(rs_a, a_voff[1], ka, ah0 + (wid + 8) * 1024);
-      big_dma<16>(rs_a, a_voff[2], ka, ah1 + wid * 1024);
-      big_dma<16>(rs_a, a_voff[3], ka, ah1 + (wid + 8) * 1024);
-      uint8_t* bd = (st == 0 ? b0 : b1) + 2 * wid * 2048;
-      big_dma<16, 0>(rs_b, b_voff, b_soff[0] + kbw, bd);
-      big_dma<16, 1024>(rs_b, b_voff, b_soff[0] + kbw, bd);           // lands at bd + 1024
-      big_dma<16, 0>(rs_b, b_voff, b_soff[1] + kbw, bd + 2048);
-      big_dma<16, 1024>(rs_b, b_voff, b_soff[1] + kbw, bd + 2048);    // lands at bd + 3072
-      big_dma<4>(rs_s, s_voff, (uint32_t)kb * 4u, (st == 0 ? s0 : s1) + (wid & 3) * 64);
+      uint8_t* ah = (st == 0 ? a0 : a1) + (q >> 1) * BG_HALF + (wid + 8 * (q & 1)) * 1024;
+      uint8_t* bd = (st == 0 ? b0 : b1) + 2 * wid * 2048 + ((q - 4) >> 1) * 2048;
+      const uint32_t kbw = (uint32_t)kb * 2048u;
+      switch (q) {
+        case 0: case 1: case 2: case 3:
+          big_dma<16>(rs_a, a_voff[q], (uint32_t)kb * 128u, ah);
+          break;
+        case 4: case 6:
+          big_dma<16, 0>(rs_b, b_voff, b_soff[(q - 4) >> 1] + kbw, bd);
+          break;
+        case 5: case 7:                            // the fragment's second half
+          big_dma<16, 1024>(rs_b, b_voff, b_soff[(q - 4) >> 1] + kbw, bd);
+          break;
+        default:
+          big_dma<4>(rs_s, s_voff, (uint32_t)kb * 4u, (st == 0 ? s0 : s1) + (wid & 3) * 64);
+      }
       asm volatile("" ::: "memory");
+    };
+    auto dma = [&](auto S, int kb) {
+#pragma unroll
+      for (int q = 0; q < kBigDmaPerBlock; ++q) dma_piece(S, kb, q);
     };
 
     // the wave's weight-scale row (a wave's columns lie in one 128-row weight block)
@@ -260,8 +268,15 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(BigArgs args,
           if (s == 28 && has_next) {
             wait_vmcnt<0>();
             big_barrier();
-            if (has_next2) dma(std::integral_constant<int, st>{}, kb + 2);
           }
+          // The copies of a block go out one piece at a time (a burst of them stalls the
+          // issuing wave until the vector memory unit takes them): pieces 0 and 1 of block
+          // kb + 2 after the barrier at step 28, pieces 2-8 of block kb + 1 at steps 0, 2,
+          // .., 12 (block 1 went out whole before the loop).  All land before step 28.
+          if ((s == 28 || s == 30) && has_next2)
+            dma_piece(std::integral_constant<int, st>{}, kb + 2, (s - 28) / 2);
+          if (s <= 12 && (s & 1) == 0 && kb >= 1 && has_next)
+            dma_piece(std::integral_constant<int, nx>{}, kb + 1, 2 + s / 2);
           // weights as the A operand: a lane holds four consecutive output columns of
           // one output row (the transposed 16x16 tile)
           pp[s & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i & 1], zero, 0,
