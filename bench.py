@@ -247,12 +247,19 @@ def main(argv=None):
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="print per-kernel average counter values of a rocprofv3 --pmc "
                          "--output-format csv run written to DIR, then exit")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print HBM bytes per dispatch of the GEMM kernels from a FETCH_SIZE "
+                         "and a WRITE_SIZE rocprofv3 --pmc run of --workload (prefill_fp8 or "
+                         "grouped_gemm_fp8), calibrated on the weight quantiser, then exit")
     a = ap.parse_args(argv)
     if a.trace_summary:
         print(trace_summary(a.trace_summary))
         return 0
     if a.pmc_summary:
         print(json.dumps(pmc_summary(a.pmc_summary), indent=1))
+        return 0
+    if a.traffic_summary:
+        print(json.dumps(traffic_summary(*a.traffic_summary, a.workload), indent=1))
         return 0
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
@@ -421,18 +428,19 @@ def gemm_source_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of a GEMM kernel from the committed rocprofv3 counter summary,
-    or None when the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "gemm_fp8_prefill_traffic.json")
+def measured_traffic(kernel, name="gemm_fp8_prefill_traffic.json"):
+    """HBM bytes per launch of a GEMM kernel from a committed rocprofv3 counter summary
+    (profiles/<name>), or None when the kernel sources changed since the counters were
+    taken."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         d = json.load(open(path))
         sha = gemm_source_sha256()
     except (OSError, ValueError):
         return None
-    if d.get("kernel_source_sha256") != sha:
+    if d.get("gemm_source_sha256") != sha or kernel not in d.get("roles", {}):
         return None
-    return round(d[kernel]["hbm_bytes_per_launch"])
+    return round(d["roles"][kernel]["hbm_bytes_per_launch"])
 
 
 def _find(dirname, suffix):
@@ -468,6 +476,49 @@ def pmc_summary(dirname):
         acc[r["Kernel_Name"][:90]][r["Counter_Name"]].append(float(r["Counter_Value"]))
     return {k: {c: {"dispatches": len(v), "avg": sum(v) / len(v)} for c, v in d.items()}
             for k, d in acc.items()}
+
+
+# weight tensors moe_quant_weight_fp8 quantises in a workload's setup, [G, R, K] each: the
+# calibration kernel of the traffic counters (reads 4 B and writes 1 B per element, plus
+# one fp32 scale per 128 x 128 block)
+CALIB_WEIGHTS = {"prefill_fp8": [(256, 4096, 7168), (256, 7168, 2048)],
+                 "grouped_gemm_fp8": [(16, 4096, 7168)]}
+CALIB_KERNEL = "moe::quant_weight_fp8_kernel"
+
+
+def traffic_summary(fetch_dir, write_dir, workload):
+    """HBM-side bytes per dispatch of every kernel in a pair of rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each counter scaled by the factor that
+    makes it read the known bytes of the calibration kernel in the same run."""
+    fetch, write = pmc_summary(fetch_dir), pmc_summary(write_dir)
+    shapes = CALIB_WEIGHTS[workload]
+    known_r = sum(g * r * k * 4 for g, r, k in shapes) / len(shapes)
+    known_w = sum(g * r * k + g * (r // 128) * (k // 128) * 4 for g, r, k in shapes) / len(shapes)
+    cal = [k for k in fetch if k.startswith(CALIB_KERNEL)][0]
+    fr = known_r / (fetch[cal]["FETCH_SIZE"]["avg"] * 1024)
+    fw = known_w / (write[cal]["WRITE_SIZE"]["avg"] * 1024)
+    out = {"calibration": {"kernel": CALIB_KERNEL, "dispatches": fetch[cal]["FETCH_SIZE"]["dispatches"],
+                           "known_read_bytes_per_dispatch": known_r,
+                           "fetch_kib": fetch[cal]["FETCH_SIZE"]["avg"], "fetch_factor": fr,
+                           "known_write_bytes_per_dispatch": known_w,
+                           "write_kib": write[cal]["WRITE_SIZE"]["avg"], "write_factor": fw},
+           "kernels": {}}
+    for k in fetch:
+        if k in write and "gemm" in k:
+            f, wv = fetch[k]["FETCH_SIZE"]["avg"], write[k]["WRITE_SIZE"]["avg"]
+            out["kernels"][k] = {"dispatches": fetch[k]["FETCH_SIZE"]["dispatches"],
+                                 "fetch_kib": f, "write_kib": wv,
+                                 "hbm_bytes_per_launch": f * 1024 * fr + wv * 1024 * fw}
+    # roles: the layer's GEMM1 (SwiGLU epilogue) and GEMM2, or the standalone GEMM
+    roles = {}
+    for k, v in out["kernels"].items():
+        if workload == "prefill_fp8" and "gemm_fp8_kernel" in k:
+            roles["gemm1" if ", true" in k else "gemm2"] = dict(v, kernel=k)
+        elif workload == "grouped_gemm_fp8" and "gemm_fp8_kernel" in k:
+            roles["gemm"] = dict(v, kernel=k)
+    out["roles"] = roles
+    out["gemm_source_sha256"] = gemm_source_sha256()
+    return out
 
 
 def bench_grouped_gemm(M, steps, warmup, settle_s=SETTLE_S):
@@ -514,7 +565,10 @@ def bench_grouped_gemm(M, steps, warmup, settle_s=SETTLE_S):
                                    "128), N=4096, K=7168, bf16 out", "group_sizes": sizes.tolist()},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
-                         "traffic": None}}
+                         "traffic": measured_traffic("gemm", "grouped_gemm_fp8_traffic.json"),
+                         "algorithmic_bytes": int(R * K + R * (K // 128) * 4 + 16 * N * K
+                                                  + 16 * (N // 128) * (K // 128) * 4
+                                                  + R * N * 2)}}
 
 
 def _time_flushed(fn, steps, warmup, settle_s=SETTLE_S):
