@@ -86,6 +86,11 @@ __device__ __forceinline__ v8bf expand8(uint32_t w, const Tab& t) {
                  (int)__builtin_amdgcn_perm(h47, l47, 0x07030602u)};
   return __builtin_bit_cast(v8bf, r);
 }
+// wait for this wave's LDS reads, then for the whole workgroup (a stage is refilled
+// right after the barrier, so no read of it may still be in flight)
+__device__ __forceinline__ void w4_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 }  // namespace
 
 template <bool SWIGLU>
@@ -185,64 +190,77 @@ __global__ __launch_bounds__(512, 1) void gemm_w4a16_kernel(W4Args args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-    // K loop: buffers hold blocks kb, kb+1, kb+2; one barrier per block publishes block
-    // kb and certifies that every wave is done with block kb-1, whose buffer is refilled.
+    // K loop: block j lives in stage j % 3.  Its last LDS reads (the operands of step 7)
+    // are made during step 6; at step 7 the workgroup waits for block j + 1 and meets at a
+    // barrier, after which stage j % 3 is free: block j + 3 goes into it (two blocks of
+    // copy latency in flight), and the wave reads block j + 1's codes, scale table and
+    // step-0 operands while block j's last MFMAs run, so the next block starts with its
+    // operands in registers.
     issue(0, 0);
     if (KB > 1) issue(1, 1);
+    if (KB > 2) issue(2, 2);
+    wait_vmcnt_upto<2 * PER_MAX>((KB > 1 ? per : 0) + (KB > 2 ? per : 0));   // block 0 landed
+    w4_lds_barrier();
+
+    v4i raw[2];
+    Tab tab;
+    auto read_codes = [&](const uint8_t* L) {
+      const int r = wid * WR + l32;
+      const uint8_t* src = L + BR_OFF + r * 64;
+      raw[0] = *reinterpret_cast<const v4i*>(src + (((2 * hf) ^ ckey(r)) << 4));
+      raw[1] = *reinterpret_cast<const v4i*>(src + (((2 * hf + 1) ^ ckey(r)) << 4));
+      tab = make_tab(reinterpret_cast<const float*>(L + SC_OFF)[r]);
+    };
+    auto expand_step = [&](int kk) { return expand8((uint32_t)raw[kk >> 2][kk & 3], tab); };
+    // MFMA step kk takes k = 64 hf + 8 kk + e from lane (l32, hf): code word 8 hf + kk of
+    // the weight row and 16-byte piece 8 hf + kk of the A row, one k order for both.
+    auto read_step = [&](const uint8_t* L, int kk, v8bf* af) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = i * 32 + l32;
+        af[i] = *reinterpret_cast<const v8bf*>(L + row * ROWB +
+                                               (((8 * hf + kk) ^ akey(row)) << 4));
+      }
+    };
+    // software pipeline over the 8 steps: while the TM MFMAs of step kk run, the wave
+    // reads the A fragments and expands the weights of step kk + 1 (of block j + 1 at
+    // step 7)
+    v8bf af[2][TM], bf[2];
+    read_codes(lds[0]);
+    read_step(lds[0], 0, af[0]);
+    bf[0] = expand_step(0);
     int st = 0;
     for (int kb = 0; kb < KB; ++kb) {
-      wait_vmcnt_upto<PER_MAX>(kb + 1 < KB ? per : 0);
-      __builtin_amdgcn_s_barrier();
-      if (kb + 2 < KB) issue(st == 0 ? 2 : st - 1, kb + 2);
       const uint8_t* L = lds[st];
-      // MFMA step kk takes k = 64 hf + 8 kk + e from lane (l32, hf): code word 8 hf + kk
-      // of the weight row and 16-byte piece 8 hf + kk of the A row, one k order for both.
-      v4i raw[2];
-      Tab tab;
-      {
-        const int r = wid * WR + l32;
-        const uint8_t* src = L + BR_OFF + r * 64;
-        raw[0] = *reinterpret_cast<const v4i*>(src + (((2 * hf) ^ ckey(r)) << 4));
-        raw[1] = *reinterpret_cast<const v4i*>(src + (((2 * hf + 1) ^ ckey(r)) << 4));
-        tab = make_tab(reinterpret_cast<const float*>(L + SC_OFF)[r]);
-      }
-      auto expand_step = [&](int kk) { return expand8((uint32_t)raw[kk >> 2][kk & 3], tab); };
-      auto read_step = [&](int kk, v8bf* af) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int row = i * 32 + l32;
-          af[i] = *reinterpret_cast<const v8bf*>(L + row * ROWB +
-                                                 (((8 * hf + kk) ^ akey(row)) << 4));
-        }
-      };
-      // software pipeline over the 8 steps: while the TM MFMAs of step kk run, the wave
-      // reads the A fragments and expands the weights of step kk + 1
-      v8bf af[2][TM], bf[2];
-      read_step(0, af[0]);
-      bf[0] = expand_step(0);
+      const int stn = st == NS - 1 ? 0 : st + 1;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int c = kk & 1;
         if (kk + 1 < 8) {
-          read_step(kk + 1, af[c ^ 1]);
+          read_step(L, kk + 1, af[c ^ 1]);
           bf[c ^ 1] = expand_step(kk + 1);
+        } else if (kb + 1 < KB) {
+          wait_vmcnt_upto<PER_MAX>(kb + 2 < KB ? per : 0);                // block kb+1 landed
+          w4_lds_barrier();
+          if (kb + 3 < KB) issue(st, kb + 3);
+          read_codes(lds[stn]);
+          read_step(lds[stn], 0, af[0]);
+          bf[0] = expand_step(0);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c], acc[i], 0, 0, 0);
         // issue order: each MFMA followed by a share of the next step's LDS reads and
         // expansion (left alone, the scheduler sinks them to their uses)
-        if (kk + 1 < 8) {
 #pragma unroll
-          for (int m = 0; m < TM; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // DS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 15 / TM + 1, 0);    // VALU
-          }
+        for (int m = 0; m < TM; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 15 / TM + 1, 0);    // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      st = st == NS - 1 ? 0 : st + 1;
+      st = stn;
     }
 
     // epilogue through LDS (stage buffers are idle): 16-byte row-contiguous stores

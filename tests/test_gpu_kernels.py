@@ -468,11 +468,14 @@ def test_gemm_fp8_dense(Mrows, K):
     assert beyond <= TOL
 
 
+@pytest.mark.parametrize("K", [128, 256, 384, 512, 1280])
 @pytest.mark.parametrize("swiglu", [False, True])
-def test_grouped_gemm_w4a16(swiglu):
-    sizes = [70, 0, 130, 5]
-    N, K = 128, 256
-    note(f"gemm w4a16 swiglu={swiglu}")
+def test_grouped_gemm_w4a16(swiglu, K):
+    """Every K-block count of the three-stage pipeline (1, 2, 3, 4 and 10 blocks) and all
+    three tile variants (<= 32, <= 64 and 128 live rows)."""
+    sizes = [70, 0, 130, 5, 40]
+    N = 128
+    note(f"gemm w4a16 swiglu={swiglu} K={K}")
     a, b, offsets, R = _gemm_case(sizes, N, K, 16, 13, swiglu)
     a_bf = a.to(torch.bfloat16)
     qb, s7 = M.moe_quant_weight_int4(b.to(dev()))
