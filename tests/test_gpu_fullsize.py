@@ -200,11 +200,15 @@ def test_fullsize_hash_w4a8_layer():
     _layer_fullsize(synth.WORKLOADS["hash_w4a8"], [0, 1, 77, 4096, 5000, 8191])
 
 
-def test_fullsize_grouped_gemm_fp8():
-    """16 groups, sizes ~ Zipf(1.1) summing to 8192, each padded to 128; N=4096, K=7168."""
+@pytest.mark.parametrize("big", ["0", "1"])
+def test_fullsize_grouped_gemm_fp8(big, monkeypatch):
+    """16 groups, sizes ~ Zipf(1.1) summing to 8192, each padded to 128; N=4096, K=7168.
+    With big = "1" the whole 256-row tiles of the largest groups (one round of 16 row
+    tiles) go to the 256 x 256-tile kernel and the rest to the 128-row kernel."""
+    monkeypatch.setenv("FP8GG_BIG_TILES", big)
     sizes = synth.zipf_group_sizes(8192, 16, 1.1, seed=0)
     N, K = 4096, 7168
-    note(f"full-size grouped GEMM sizes={sizes.tolist()} N={N} K={K}")
+    note(f"full-size grouped GEMM sizes={sizes.tolist()} N={N} K={K} big={big}")
     padded = -(-sizes // 128) * 128
     offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
     R = int(offsets[-1])

@@ -143,6 +143,17 @@ def test_layer_renorm(mode):
                                   m_align=16, seed=9), renorm=True)
 
 
+def test_layer_big_tiles(monkeypatch):
+    """Few large experts (about 770 rows each): with FP8GG_BIG_TILES=1 the layer's GEMM1
+    (SwiGLU, 32 column tiles, so 8 row tiles a round) sends each expert's leading 256-row
+    tiles to the 256 x 256-tile kernel; the layer must still match the per-step entry
+    points bit for bit and the oracle on sampled tokens."""
+    monkeypatch.setenv("FP8GG_BIG_TILES", "1")
+    w = synth.Workload("big_tiles_fp8", T=1024, d=2048, E=4, k=3, I=4096, mode="fp8",
+                       m_align=16, seed=5)
+    run_layer_case(w, tokens=[0, 1, 2, 100, 511, 512, 700, 1000, 1022, 1023])
+
+
 def test_layer_small_fp8_many_experts():
     run_layer_case(synth.Workload("small_fp8_e64", T=200, d=384, E=64, k=6, I=128, mode="fp8",
                                   m_align=32, seed=3))
