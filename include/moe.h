@@ -220,7 +220,13 @@ int moe_quant_weight_int4(const float *w, int G, int N, int K, uint8_t *q, float
  * first 2^32 - 256 bytes of A (checked as R_cap * K when a_rows is NULL; with a_rows
  * the caller guarantees it for the rows a_rows names).
  * C and sC must not overlap sB (checked: the kernel reads sB through the scalar cache)
- * nor any other input (not checked). */
+ * nor any other input (not checked).
+ * Kernel choice: with FP8GG_BIG_TILES=1 in the environment (read at each call), groups
+ * that average at least 256 rows (R_cap / G here, cap for the masked form, M for
+ * gemm_fp8, the layer's row bound per expert in moe_layer_fwd) with K / 128 even have
+ * their whole 256-row tiles computed by a 256 x 256-tile kernel launched first on the
+ * same stream; the definition above holds either way (the same promotion order, so
+ * bit-identical outputs in every tested case).  Unset or any other value: one kernel. */
 int grouped_gemm_fp8(const uint8_t *A, const float *sA, const int32_t *a_rows, int a_row_div,
                      const uint8_t *B, const float *sB, const int32_t *offsets, int G,
                      int R_cap, int N, int K, int epilogue, moe_dtype out_dt, void *C,
