@@ -3,43 +3,85 @@
 //
 // A gather, not a scatter: each token reads its k expert rows and sums them in fp32
 // in slot order j = 0..k-1, so the result is deterministic (no atomics).  One
-// workgroup per token; each thread handles 8 consecutive columns (16-byte bf16 loads).
+// workgroup per token; each thread handles 8 consecutive columns (16-byte loads).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
+
+// the k rows of a chunk summed in slot order (the same order and roundings whatever the
+// batching below); o row loads of one batch are all issued before the first add
+template <bool OBF16, int KU>
+__device__ __forceinline__ void add_rows(const void* __restrict__ o, const int* rows,
+                                         const float* wv, int n, int d, int c, float* acc) {
+  constexpr int VW = OBF16 ? 1 : 2;               // 16-byte loads per slot and chunk
+  v4i raw[KU][VW];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {                  // slots past n or dropped read row 0
+    const size_t r = (size_t)max(u < n ? rows[u] : 0, 0);
+    if (OBF16) {
+      raw[u][0] = *reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(o) + r * d + c * 8);
+    } else {
+      const float* p = static_cast<const float*>(o) + r * d + c * 8;
+      raw[u][0] = *reinterpret_cast<const v4i*>(p);
+      raw[u][VW - 1] = *reinterpret_cast<const v4i*>(p + 4);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    if (u >= n || rows[u] < 0) continue;          // the same for the whole workgroup
+    float v[8];
+    if (OBF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32((uint16_t)(raw[u][0][i] & 0xFFFF));
+        v[2 * i + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[u][0][i] >> 16));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = __int_as_float(raw[u][0][i]);
+        v[4 + i] = __int_as_float(raw[u][VW - 1][i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wv[u], v[i], acc[i]);
+  }
+}
 
 template <bool OBF16, bool YBF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o,
                                                       const int32_t* __restrict__ row_of_slot,
                                                       const float* __restrict__ w, int k, int d,
                                                       void* __restrict__ y) {
+  constexpr int KU = 8;                           // slots per batch of loads
   const int t = blockIdx.x;
   const int chunks = d / 8;
+  // k <= KU (every top-k here): the token's rows and weights once, in scalar registers
+  int rows0[KU];
+  float w0[KU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int jc = min(u, k - 1);
+    rows0[u] = row_of_slot[(size_t)t * k + jc];
+    w0[u] = w[(size_t)t * k + jc];
+  }
   for (int c = threadIdx.x; c < chunks; c += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int row = row_of_slot[(size_t)t * k + j];
-      if (row < 0) continue;
-      const float wj = w[(size_t)t * k + j];
-      float v[8];
-      if (OBF16) {
-        v4i raw = *reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(o) +
-                                                 (size_t)row * d + c * 8);
+    if (k <= KU) {
+      add_rows<OBF16, KU>(o, rows0, w0, k, d, c, acc);
+    } else {
+      for (int j0 = 0; j0 < k; j0 += KU) {
+        int rows[KU];
+        float wv[KU];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = bf16_to_f32((uint16_t)(raw[i] & 0xFFFF));
-          v[2 * i + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[i] >> 16));
+        for (int u = 0; u < KU; ++u) {
+          const int jc = min(j0 + u, k - 1);
+          rows[u] = row_of_slot[(size_t)t * k + jc];
+          wv[u] = w[(size_t)t * k + jc];
         }
-      } else {
-        const float* p = static_cast<const float*>(o) + (size_t)row * d + c * 8;
-        v4f a = *reinterpret_cast<const v4f*>(p);
-        v4f b = *reinterpret_cast<const v4f*>(p + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+        add_rows<OBF16, KU>(o, rows, wv, min(KU, k - j0), d, c, acc);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
     }
     if (YBF16) {
       v4i out;
