@@ -5,25 +5,30 @@
 // matrix core into a fresh fp32 partial and promoted with its two scales, the
 // two-level accumulation of qidao123.com day 3), for the whole 256-row tiles of large
 // groups.  Why a second kernel: in the 128 x 256 tiles of gemm_fp8_kernel every CU pulls
-// 48 KB of operands per 128-deep block for 1024 cycles of matrix work, and the measured
-// feed of a CU's vector memory path (~28 B per cycle with this access pattern) is what
-// bounds those tiles.  A 256 x 256 tile pulls 64 KB for 2048 cycles of matrix work.
+// 48 KB of operands per 128-deep block for 1024 cycles of matrix work, near what a CU's
+// vector memory path takes in (about 40-45 B per cycle for 16-byte-per-lane loads); a
+// 256 x 256 tile pulls 64 KB for 2048 cycles of matrix work.  Measured on MI355X it is
+// nevertheless slower than the 128-row kernel, so callers get it only on request.
 //
 // gfx950 mapping
 //   * 512 threads = 8 waves, two per SIMD, as a 2 x 4 grid: wave (wr, wc) computes tile
 //     rows wr*128 .. +128 against weight rows wc*64 .. +64 (SwiGLU: gate rows wc*32 .. +32
-//     and the up rows of the same output columns), 32 MFMA tiles of 16 x 16 per block.
-//   * Both operands reach LDS by direct global->LDS DMA, two stages: the activation rows
-//     (gathered through a_rows, 16-byte XOR swizzle as in gemm_fp8_kernel) as two
-//     128-row halves, the 16 fragment-major weight fragments of the tile (2 KB each, in
-//     the order the MFMA takes them), and the tile rows' scales of the block.  Each stage
-//     piece is an LDS object of its own, so the compiler tells a copy into one stage from
-//     reads of the other.  A block's copies go out at the block's start, into the stage
-//     the previous block freed, and land before the block's closing barrier; they are
-//     the only vector memory operations in the loop, so that barrier waits for zero.
-//   * Per block a wave reads its 4 weight fragments once and its 8 activation fragments
-//     one ahead of their MFMAs; each MFMA's partial is promoted one step behind (the
-//     block's last one at its end) with the row scale times the weight-block scale.
+//     and the up rows of the same output columns), 32 MFMA tiles of 16 x 16 per block,
+//     128 accumulator registers.
+//   * Both operands reach LDS by direct global->LDS DMA, two stages of 64 KB: the
+//     activation rows (gathered through a_rows, 16-byte XOR swizzle as in
+//     gemm_fp8_kernel), the tile's 16 fragment-major weight fragments (2 KB each, in the
+//     order the MFMA takes them) and the rows' scales of the block.  The tile's two
+//     weight-scale rows for every K block are copied to LDS once per tile.
+//   * The barrier that publishes block kb+1 sits at step 28 of block kb's 32 MFMA steps
+//     (the block's last LDS read of its own stage is at step 24); steps 29-31 refill each
+//     weight fragment right after its last use and read block kb+1's first activation
+//     fragment, so a block starts with its operands in registers.  The copies of block
+//     kb+2 go out one piece per step after that barrier, into the stage it freed.  They
+//     are issued as inline asm and the kernel waits for them itself (vmcnt(0) before each
+//     publishing barrier): they are the only vector memory operations in the loop.
+//   * Each MFMA's partial is promoted one step behind, after the next MFMA has been
+//     issued, with the row scale times the weight-block scale.
 //   * Tiles: only whole 256-row tiles, and only whole rounds of the grid (big_cut: the
 //     rest goes to gemm_fp8_kernel, launched after this one with the same cut).  Runs of
 //     two row tiles are walked column tile by column tile, so the 32 tiles one XCD holds
