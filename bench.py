@@ -262,7 +262,7 @@ def main(argv=None):
         print(json.dumps(traffic_summary(*a.traffic_summary, a.workload), indent=1))
         return 0
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "this implementation runs on exactly one GPU; --gpus must be 1 "
                                    "(multi-GPU expert parallelism is not built)"}))
         return 2
 
