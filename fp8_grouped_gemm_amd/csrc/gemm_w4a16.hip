@@ -174,14 +174,22 @@ __global__ __launch_bounds__(512, 1) void gemm_w4a16_kernel(W4Args args) {
     const uint32_t m_a = lds0 + (uint32_t)wid * (A_IN * 1024);
     const uint32_t m_b = lds0 + BR_OFF + (uint32_t)wid * (B_IN * 1024);
     const uint32_t m_s = lds0 + SC_OFF + (uint32_t)wid * (WR * 4);
-    auto issue = [&](int st, int kb) {
+    // piece q of the copies of block kb into stage st (this wave's A rows, then its codes,
+    // then the scales); pieces this wave does not have are skipped, so a block is `per`
+    // copies for every wave
+    auto issue_piece = [&](int st, int kb, int q) {
       const uint32_t so = (uint32_t)st * STAGE;
+      if (q < A_IN) {
+        if (q < a_cnt) dma16(a_src[q] + (size_t)kb * ROWB, m_a + so + q * 1024);
+      } else if (q < A_IN + B_IN) {
+        dma16(b_src[q - A_IN] + (size_t)kb * 64, m_b + so + (q - A_IN) * 1024);
+      } else if (scales) {
+        dma4(s_src + kb, m_s + so);
+      }
+    };
+    auto issue = [&](int st, int kb) {
 #pragma unroll
-      for (int i = 0; i < A_IN; ++i)
-        if (i < a_cnt) dma16(a_src[i] + (size_t)kb * ROWB, m_a + so + i * 1024);
-#pragma unroll
-      for (int i = 0; i < B_IN; ++i) dma16(b_src[i] + (size_t)kb * 64, m_b + so + i * 1024);
-      if (scales) dma4(s_src + kb, m_s + so);
+      for (int q = 0; q < PER_MAX; ++q) issue_piece(st, kb, q);
     };
 
     v16f acc[TM];
@@ -190,12 +198,13 @@ __global__ __launch_bounds__(512, 1) void gemm_w4a16_kernel(W4Args args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-    // K loop: block j lives in stage j % 3.  Its last LDS reads (the operands of step 7)
-    // are made during step 6; at step 7 the workgroup waits for block j + 1 and meets at a
-    // barrier, after which stage j % 3 is free: block j + 3 goes into it (two blocks of
-    // copy latency in flight), and the wave reads block j + 1's codes, scale table and
-    // step-0 operands while block j's last MFMAs run, so the next block starts with its
-    // operands in registers.
+    // K loop: block j lives in stage j % 3.  At step 6 of block j the workgroup waits for
+    // block j + 1 and meets at a barrier, after which stage j % 3 is free, and the wave
+    // reads block j + 1's codes, scale table and first operands while block j's last
+    // MFMAs run, so the next block starts with its operands in registers.  Block j + 3
+    // goes into the freed stage one copy per step over steps 0-6 of block j + 1 (a burst
+    // of a wave's copies stalls it until the vector memory unit takes them); it is waited
+    // for at step 6 of block j + 2.
     issue(0, 0);
     if (KB > 1) issue(1, 1);
     if (KB > 2) issue(2, 2);
@@ -223,34 +232,44 @@ __global__ __launch_bounds__(512, 1) void gemm_w4a16_kernel(W4Args args) {
       }
     };
     // software pipeline over the 8 steps: while the TM MFMAs of step kk run, the wave
-    // reads the A fragments and expands the weights of step kk + 1 (of block j + 1 at
-    // step 7)
-    v8bf af[2][TM], bf[2];
+    // reads the A fragments of step kk + 2 (a ring of four, so a read has two steps to
+    // land) and expands the weights of step kk + 1.  The block's last LDS reads are made
+    // at step 5, so the barrier that publishes block kb + 1 sits at step 6; steps 6 and 7
+    // read block kb + 1's codes, scale table and first two A fragments.
+    v8bf af[4][TM], bf[2];
     read_codes(lds[0]);
     read_step(lds[0], 0, af[0]);
+    read_step(lds[0], 1, af[1]);
     bf[0] = expand_step(0);
     int st = 0;
     for (int kb = 0; kb < KB; ++kb) {
       const uint8_t* L = lds[st];
       const int stn = st == NS - 1 ? 0 : st + 1;
+      const int stp = st == 0 ? NS - 1 : st - 1;   // the stage block kb - 1 freed
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int c = kk & 1;
-        if (kk + 1 < 8) {
-          read_step(L, kk + 1, af[c ^ 1]);
+        if (kk < PER_MAX && kb >= 1 && kb + 2 < KB) issue_piece(stp, kb + 2, kk);
+        if (kk < 6) {
+          read_step(L, kk + 2, af[(kk + 2) & 3]);
           bf[c ^ 1] = expand_step(kk + 1);
+        } else if (kk == 6) {
+          bf[1] = expand_step(7);                  // the last use of this block's codes
+          if (kb + 1 < KB) {
+            wait_vmcnt_upto<PER_MAX>(kb + 2 < KB ? per : 0);              // block kb+1 landed
+            w4_lds_barrier();
+            read_codes(lds[stn]);
+            read_step(lds[stn], 0, af[0]);
+          }
         } else if (kb + 1 < KB) {
-          wait_vmcnt_upto<PER_MAX>(kb + 2 < KB ? per : 0);                // block kb+1 landed
-          w4_lds_barrier();
-          if (kb + 3 < KB) issue(st, kb + 3);
-          read_codes(lds[stn]);
-          read_step(lds[stn], 0, af[0]);
-          bf[0] = expand_step(0);
+          bf[0] = expand_step(0);                  // block kb + 1, codes read at step 6
+          read_step(lds[stn], 1, af[1]);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c], acc[i], 0, 0, 0);
-        // issue order: each MFMA followed by a share of the next step's LDS reads and
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 3][i], bf[c], acc[i], 0, 0,
+                                                           0);
+        // issue order: each MFMA followed by a share of the next steps' LDS reads and
         // expansion (left alone, the scheduler sinks them to their uses)
 #pragma unroll
         for (int m = 0; m < TM; ++m) {
@@ -280,7 +299,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w4a16_kernel(W4Args args) {
             const float up = __shfl_xor(acc[i][r], 16, 64);
             if (l32 < 16) {
               const int tcol = wid * 16 + l32;
-              const float hv = silu(acc[i][r]) * up;
+              const float hv = silu_fast(acc[i][r]) * up;   // rounded to bf16 next
               *reinterpret_cast<uint16_t*>(ot + trow * OB + tcol * 2) = f32_to_bf16(hv);
             }
           } else {
