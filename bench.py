@@ -647,36 +647,50 @@ def bench_masked_gemm(M, steps, warmup, settle_s=SETTLE_S):
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
 
 
+def _stage_loop(names, one, steps):
+    """Average HIP-event time of each named stage.  one(rec) runs the stages in order on
+    torch's current stream and calls rec() after each.  After one warm pass and one
+    synchronisation the timed passes are queued back to back and synchronised once at the
+    end, so the host's launch time does not fall between the events of a short stage."""
+    def run(evs):
+        nxt = iter(evs[1:])
+        evs[0].record()
+        one(lambda: next(nxt).record())
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]  # noqa: E731
+    run(mk())                               # first pass warms the allocator
+    torch.cuda.synchronize()
+    passes = []
+    for _ in range(steps):
+        evs = mk()
+        run(evs)
+        passes.append(evs)
+    torch.cuda.synchronize()
+    return {n: sum(e[i].elapsed_time(e[i + 1]) for e in passes) / steps
+            for i, n in enumerate(names)}
+
+
 def stage_times(M, w, inp, weights, steps):
     """Average time of each step of the layer, run through the individual C entry points
     on torch's current stream and bracketed by HIP events."""
-    dev = inp["x"].device
     x = inp["x"]
-    names = ["route", "dispatch", "quant", "gemm1", "gemm2", "combine"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    acc = {n: 0.0 for n in names}
     R = M.moe_rows_bound(w.T, w.k, w.E, w.m_align)
-    for it in range(steps + 1):
-        ev[0].record()
+
+    def one(rec):
         idx, gw, _ = M.moe_route(x, inp["w_router"], inp["bias"], w.k)
-        ev[1].record()
+        rec()
         counts, offsets, ros, sor = M.moe_dispatch(idx, w.E, w.m_align)
-        ev[2].record()
+        rec()
         qx, sx = M.moe_quant_fp8(x)
-        ev[3].record()
+        rec()
         hq, sh = M.grouped_gemm_fp8(qx, sx, weights["w13"], weights["s13"], offsets, R, w.I,
                                     swiglu=True, a_rows=sor, a_row_div=w.k)
-        ev[4].record()
+        rec()
         o = M.grouped_gemm_fp8(hq, sh, weights["w2"], weights["s2"], offsets, R, w.d)
-        ev[5].record()
+        rec()
         M.moe_combine(o, ros, gw, w.T, w.k)
-        ev[6].record()
-        torch.cuda.synchronize()
-        if it == 0:
-            continue        # first pass warms the allocator
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    return {n: acc[n] / steps for n in names}
+        rec()
+
+    return _stage_loop(["route", "dispatch", "quant", "gemm1", "gemm2", "combine"], one, steps)
 
 
 def stage_times_masked(M, w, inp, weights, steps, cap):
@@ -684,30 +698,23 @@ def stage_times_masked(M, w, inp, weights, steps, cap):
     points: route -> masked dispatch -> quant-gather into [E, C, d] -> masked GEMM1 ->
     masked GEMM2 -> combine."""
     x = inp["x"]
-    names = ["route", "dispatch", "quant", "gemm1", "gemm2", "combine"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    acc = {n: 0.0 for n in names}
-    for it in range(steps + 1):
-        ev[0].record()
+
+    def one(rec):
         idx, gw, _ = M.moe_route(x, inp["w_router"], inp["bias"], w.k)
-        ev[1].record()
+        rec()
         counts, ros, sor = M.moe_dispatch_masked(idx, w.E, cap)
-        ev[2].record()
+        rec()
         qa, sa = M.moe_quant_fp8(x, sor, w.k, w.E * cap)
-        ev[3].record()
+        rec()
         hq, sh = M.grouped_gemm_fp8_masked(qa, sa, weights["w13"], weights["s13"], counts, cap,
                                            w.I, swiglu=True)
-        ev[4].record()
+        rec()
         o = M.grouped_gemm_fp8_masked(hq, sh, weights["w2"], weights["s2"], counts, cap, w.d)
-        ev[5].record()
+        rec()
         M.moe_combine(o, ros, gw, w.T, w.k)
-        ev[6].record()
-        torch.cuda.synchronize()
-        if it == 0:
-            continue
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    return {n: acc[n] / steps for n in names}
+        rec()
+
+    return _stage_loop(["route", "dispatch", "quant", "gemm1", "gemm2", "combine"], one, steps)
 
 
 def stage_times_w4a8(M, w, inp, weights, steps):
@@ -715,60 +722,46 @@ def stage_times_w4a8(M, w, inp, weights, steps):
     route_hash -> dispatch -> 1x128 quant -> GEMM1 with the token gather -> GEMM2 ->
     combine."""
     x = inp["x"]
-    names = ["route", "dispatch", "quant", "gemm1", "gemm2", "combine"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    acc = {n: 0.0 for n in names}
     R = M.moe_rows_bound(w.T, w.k, w.E, w.m_align)
-    for it in range(steps + 1):
-        ev[0].record()
+
+    def one(rec):
         idx, gw = M.moe_route_hash(inp["token_ids"], w.E)
-        ev[1].record()
+        rec()
         counts, offsets, ros, sor = M.moe_dispatch(idx, w.E, w.m_align)
-        ev[2].record()
+        rec()
         qx, sx = M.moe_quant_fp8(x)
-        ev[3].record()
+        rec()
         hq, sh = M.grouped_gemm_w4a8(qx, sx, weights["w13"], weights["s13"], offsets, R, w.I,
                                      swiglu=True, a_rows=sor, a_row_div=w.k)
-        ev[4].record()
+        rec()
         o = M.grouped_gemm_w4a8(hq, sh, weights["w2"], weights["s2"], offsets, R, w.d)
-        ev[5].record()
+        rec()
         M.moe_combine(o, ros, gw, w.T, w.k)
-        ev[6].record()
-        torch.cuda.synchronize()
-        if it == 0:
-            continue
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    return {n: acc[n] / steps for n in names}
+        rec()
+
+    return _stage_loop(["route", "dispatch", "quant", "gemm1", "gemm2", "combine"], one, steps)
 
 
 def stage_times_w4a16(M, w, inp, weights, steps):
     """Stage times of the hash-routed W4A16 layer through the individual C entry points
     (route_hash -> dispatch -> GEMM1 with the token gather -> GEMM2 -> combine)."""
     x = inp["x"]
-    names = ["route", "dispatch", "gemm1", "gemm2", "combine"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    acc = {n: 0.0 for n in names}
     R = M.moe_rows_bound(w.T, w.k, w.E, w.m_align)
-    for it in range(steps + 1):
-        ev[0].record()
+
+    def one(rec):
         idx, gw = M.moe_route_hash(inp["token_ids"], w.E)
-        ev[1].record()
+        rec()
         counts, offsets, ros, sor = M.moe_dispatch(idx, w.E, w.m_align)
-        ev[2].record()
+        rec()
         h = M.grouped_gemm_w4a16(x, weights["w13"], weights["s13"], offsets, R, w.I,
                                  swiglu=True, a_rows=sor, a_row_div=w.k)
-        ev[3].record()
+        rec()
         o = M.grouped_gemm_w4a16(h, weights["w2"], weights["s2"], offsets, R, w.d)
-        ev[4].record()
+        rec()
         M.moe_combine(o, ros, gw, w.T, w.k)
-        ev[5].record()
-        torch.cuda.synchronize()
-        if it == 0:
-            continue
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    return {n: acc[n] / steps for n in names}
+        rec()
+
+    return _stage_loop(["route", "dispatch", "gemm1", "gemm2", "combine"], one, steps)
 
 
 if __name__ == "__main__":

@@ -68,7 +68,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
   }
   for (int c = threadIdx.x; c < chunks; c += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (k <= KU) {
+    // a batch as large as k needs (no loads for slots past k)
+    if (k == 1) {
+      add_rows<OBF16, 1>(o, rows0, w0, k, d, c, acc);
+    } else if (k == 2) {
+      add_rows<OBF16, 2>(o, rows0, w0, k, d, c, acc);
+    } else if (k <= 4) {
+      add_rows<OBF16, 4>(o, rows0, w0, k, d, c, acc);
+    } else if (k <= KU) {
       add_rows<OBF16, KU>(o, rows0, w0, k, d, c, acc);
     } else {
       for (int j0 = 0; j0 < k; j0 += KU) {

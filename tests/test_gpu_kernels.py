@@ -517,6 +517,9 @@ def test_grouped_gemm_f32(swiglu):
     (99, 4, 16, 20),      # some slots dropped
     (64, 10, 32, 3),      # two load batches of slots; tokens with every slot dropped
     (50, 1, 8, 0),        # one slot per token, no capacity limit
+    (70, 2, 8, 0),        # the two-slot batch
+    (33, 6, 12, 5),       # a partly used eight-slot batch, with drops
+    (40, 8, 16, 0),       # a full eight-slot batch
 ])
 @pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32])
 def test_combine(o_dtype, T, k, E, cap):
