@@ -296,7 +296,13 @@ __global__ __launch_bounds__(512, 1) void gemm_w4a16_kernel(W4Args args) {
         for (int r = 0; r < 16; ++r) {
           const int trow = i * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
           if (SWIGLU) {
-            const float up = __shfl_xor(acc[i][r], 16, 64);
+            // the up value of lane l32 < 16 sits in lane l32 + 16: a row swap on the
+            // VALU (the second result holds, in lanes 0-15 and 32-47, the values of
+            // lanes 16-31 and 48-63)
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][r]),
+                                                             __float_as_uint(acc[i][r]), false,
+                                                             false);
+            const float up = __uint_as_float(sw[1]);
             if (l32 < 16) {
               const int tcol = wid * 16 + l32;
               const float hv = silu_fast(acc[i][r]) * up;   // rounded to bf16 next
