@@ -49,15 +49,16 @@ __device__ __forceinline__ void add_rows(const void* __restrict__ o, const int* 
   }
 }
 
-template <bool OBF16, bool YBF16>
+template <bool OBF16, bool YBF16, int KU>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o,
                                                       const int32_t* __restrict__ row_of_slot,
                                                       const float* __restrict__ w, int k, int d,
                                                       void* __restrict__ y) {
-  constexpr int KU = 8;                           // slots per batch of loads
+  // KU: slots per batch of loads (the launcher picks the smallest of 1, 2, 4, 8 that
+  // holds k, or 8 with batches for larger k)
   const int t = blockIdx.x;
   const int chunks = d / 8;
-  // k <= KU (every top-k here): the token's rows and weights once, in scalar registers
+  // k <= KU: the token's rows and weights once, in scalar registers
   int rows0[KU];
   float w0[KU];
 #pragma unroll
@@ -68,14 +69,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
   }
   for (int c = threadIdx.x; c < chunks; c += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // a batch as large as k needs (no loads for slots past k)
-    if (k == 1) {
-      add_rows<OBF16, 1>(o, rows0, w0, k, d, c, acc);
-    } else if (k == 2) {
-      add_rows<OBF16, 2>(o, rows0, w0, k, d, c, acc);
-    } else if (k <= 4) {
-      add_rows<OBF16, 4>(o, rows0, w0, k, d, c, acc);
-    } else if (k <= KU) {
+    if (k <= KU) {
       add_rows<OBF16, KU>(o, rows0, w0, k, d, c, acc);
     } else {
       for (int j0 = 0; j0 < k; j0 += KU) {
@@ -105,19 +99,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
   }
 }
 
+template <int KU>
+void launch_combine_ku(const void* o, bool o_bf16, const int32_t* row_of_slot, const float* w,
+                       int T, int k, int d, void* y, bool y_bf16, hipStream_t s) {
+  dim3 grid(T), block(256);
+  if (o_bf16 && y_bf16)
+    hipLaunchKernelGGL((combine_kernel<true, true, KU>), grid, block, 0, s, o, row_of_slot, w,
+                       k, d, y);
+  else if (o_bf16)
+    hipLaunchKernelGGL((combine_kernel<true, false, KU>), grid, block, 0, s, o, row_of_slot, w,
+                       k, d, y);
+  else if (y_bf16)
+    hipLaunchKernelGGL((combine_kernel<false, true, KU>), grid, block, 0, s, o, row_of_slot, w,
+                       k, d, y);
+  else
+    hipLaunchKernelGGL((combine_kernel<false, false, KU>), grid, block, 0, s, o, row_of_slot,
+                       w, k, d, y);
+}
+
 hipError_t launch_combine(const void* o, bool o_bf16, const int32_t* row_of_slot,
                           const float* w, int T, int k, int d, void* y, bool y_bf16,
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid(T), block(256);
-  if (o_bf16 && y_bf16)
-    hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, o, row_of_slot, w, k, d, y);
-  else if (o_bf16)
-    hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, o, row_of_slot, w, k, d, y);
-  else if (y_bf16)
-    hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, o, row_of_slot, w, k, d, y);
+  if (k == 1)
+    launch_combine_ku<1>(o, o_bf16, row_of_slot, w, T, k, d, y, y_bf16, s);
+  else if (k == 2)
+    launch_combine_ku<2>(o, o_bf16, row_of_slot, w, T, k, d, y, y_bf16, s);
+  else if (k <= 4)
+    launch_combine_ku<4>(o, o_bf16, row_of_slot, w, T, k, d, y, y_bf16, s);
   else
-    hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, o, row_of_slot, w, k, d, y);
+    launch_combine_ku<8>(o, o_bf16, row_of_slot, w, T, k, d, y, y_bf16, s);
   return hipGetLastError();
 }
 
