@@ -8,6 +8,7 @@ step runs in the library's HIP kernels; nothing is computed in Python.
 from __future__ import annotations
 
 import ctypes as C
+import functools
 from typing import Optional
 
 import torch
@@ -56,6 +57,26 @@ def _lib_():
     return _lib.load()
 
 
+def _on_tensor_device(fn):
+    """Run fn with the device of its GPU tensor arguments (and of the tensors in a dict
+    argument, such as the layer's weights) current.  The library checks and launches on
+    the current HIP device, and the stream passed in belongs to the tensors' device, so
+    the two must agree; tensors on different GPUs are refused."""
+    @functools.wraps(fn)
+    def call(*args, **kwargs):
+        flat = []
+        for a in (*args, *kwargs.values()):
+            flat.extend(a.values() if isinstance(a, dict) else (a,))
+        devs = {a.device for a in flat if isinstance(a, torch.Tensor) and a.is_cuda}
+        if len(devs) > 1:
+            raise ValueError(f"{fn.__name__}: tensors on different devices {sorted(map(str, devs))}")
+        if not devs:
+            return fn(*args, **kwargs)
+        with torch.cuda.device(devs.pop()):
+            return fn(*args, **kwargs)
+    return call
+
+
 # --------------------------------------------------------------- host helpers
 
 def moe_device_supported(device: int = 0) -> bool:
@@ -74,6 +95,7 @@ def moe_rows_bound(T: int, k: int, E: int, m_align: int) -> int:
 
 # -------------------------------------------------------------------- routing
 
+@_on_tensor_device
 def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor, k: int,
               renorm: bool = False, use_workspace: bool = True):
     """Router logits + biased softmax top-k.  Returns (topk_idx, topk_w, logits).
@@ -92,6 +114,7 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor, k: in
     return idx, w, logits
 
 
+@_on_tensor_device
 def moe_route_noalloc(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor, k: int,
                       renorm: bool = False, out=None):
     """moe_route with the split-K partials in the library's static device scratch (no
@@ -115,6 +138,7 @@ def moe_route_workspace_size(T: int, d: int, E: int, dtype=torch.bfloat16) -> in
     return _lib_().moe_route_workspace_size(T, d, E, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
 
 
+@_on_tensor_device
 def moe_route_from_logits(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,
                           renorm: bool = False):
     T, E = logits.shape
@@ -127,6 +151,7 @@ def moe_route_from_logits(logits: torch.Tensor, bias: Optional[torch.Tensor], k:
     return idx, w
 
 
+@_on_tensor_device
 def moe_route_hash(token_ids: torch.Tensor, E: int):
     T = token_ids.shape[0]
     dev = token_ids.device
@@ -137,6 +162,7 @@ def moe_route_hash(token_ids: torch.Tensor, E: int):
     return idx, w
 
 
+@_on_tensor_device
 def moe_dispatch(topk_idx: torch.Tensor, E: int, m_align: int, capacity: int = 0):
     """Returns (counts [E], offsets [E+1], row_of_slot [T*k], slot_of_row [rows_bound])."""
     T, k = topk_idx.shape
@@ -152,6 +178,7 @@ def moe_dispatch(topk_idx: torch.Tensor, E: int, m_align: int, capacity: int = 0
     return counts, offsets, ros, sor
 
 
+@_on_tensor_device
 def moe_dispatch_masked(topk_idx: torch.Tensor, E: int, capacity: int):
     """Fixed-capacity layout.  Returns (counts [E], row_of_slot [T*k], slot_of_row [E*C])."""
     T, k = topk_idx.shape
@@ -167,6 +194,7 @@ def moe_dispatch_masked(topk_idx: torch.Tensor, E: int, capacity: int):
 
 # --------------------------------------------------------------- quantisation
 
+@_on_tensor_device
 def moe_quant_fp8(x: torch.Tensor, src_row: Optional[torch.Tensor] = None, src_div: int = 1,
                   rows_out: Optional[int] = None):
     """1x128 e4m3 quantisation; returns (codes uint8 [rows_out, K], scales fp32)."""
@@ -180,6 +208,7 @@ def moe_quant_fp8(x: torch.Tensor, src_row: Optional[torch.Tensor] = None, src_d
     return q, s
 
 
+@_on_tensor_device
 def moe_quant_weight_fp8(w: torch.Tensor):
     G, N, K = w.shape
     dev = w.device
@@ -190,17 +219,20 @@ def moe_quant_weight_fp8(w: torch.Tensor):
     return q, s
 
 
+@_on_tensor_device
 def moe_pack_weight_fp8(q: torch.Tensor):
     """e4m3 codes [G, N, K] (or [N, K]) -> the fragment-major layout the FP8 GEMMs read
     (same shape and byte count; see moe_pack_weight_fp8 in include/moe.h)."""
     q3 = q if q.dim() == 3 else q[None]
     G, N, K = q3.shape
+    q3 = q3.contiguous()                  # kept alive until the launch is enqueued
     out = torch.empty_like(q3)
-    _lib.check(_lib_().moe_pack_weight_fp8(_ptr(q3.contiguous()), G, N, K, _ptr(out),
-                                           _stream(q.device)), "moe_pack_weight_fp8")
+    _lib.check(_lib_().moe_pack_weight_fp8(_ptr(q3), G, N, K, _ptr(out), _stream(q.device)),
+               "moe_pack_weight_fp8")
     return out if q.dim() == 3 else out[0]
 
 
+@_on_tensor_device
 def moe_quant_weight_int4(w: torch.Tensor):
     G, N, K = w.shape
     dev = w.device
@@ -211,6 +243,7 @@ def moe_quant_weight_int4(w: torch.Tensor):
     return q, s
 
 
+@_on_tensor_device
 def moe_pack_weight_int4(q: torch.Tensor, s7: torch.Tensor):
     """int4 codes [G, N, K/2] + scales [G, N, K/128] (moe_quant_weight_int4) -> the
     fragment-major order grouped_gemm_w4a8 reads (same shapes and byte counts)."""
@@ -224,6 +257,7 @@ def moe_pack_weight_int4(q: torch.Tensor, s7: torch.Tensor):
 
 # --------------------------------------------------------------- grouped GEMM
 
+@_on_tensor_device
 def grouped_gemm_fp8(A, sA, B, sB, offsets, R_cap: int, N: int, swiglu: bool = False,
                      a_rows: Optional[torch.Tensor] = None, a_row_div: int = 1):
     """B: weight codes packed by moe_pack_weight_fp8.  Returns C bf16 [R_cap, N] (plain)
@@ -245,6 +279,7 @@ def grouped_gemm_fp8(A, sA, B, sB, offsets, R_cap: int, N: int, swiglu: bool = F
     return (Cc, sC) if swiglu else Cc
 
 
+@_on_tensor_device
 def grouped_gemm_w4a8(A, sA, B, s7, offsets, R_cap: int, N: int, swiglu: bool = False,
                       a_rows: Optional[torch.Tensor] = None, a_row_div: int = 1):
     """4-bit weights (packed by moe_pack_weight_int4) on the FP8 matrix core.  Returns C bf16
@@ -266,6 +301,7 @@ def grouped_gemm_w4a8(A, sA, B, s7, offsets, R_cap: int, N: int, swiglu: bool = 
     return (Cc, sC) if swiglu else Cc
 
 
+@_on_tensor_device
 def grouped_gemm_fp8_masked(A, sA, B, sB, counts, cap: int, N: int, swiglu: bool = False):
     """Fixed-capacity layout: A [G*cap, K]; group g owns rows [g*cap, g*cap + counts[g]).
     Returns C bf16 [G*cap, N] (plain) or (codes e4m3 [G*cap, N], sC [G*cap, N/128])."""
@@ -287,6 +323,7 @@ def grouped_gemm_fp8_masked(A, sA, B, sB, counts, cap: int, N: int, swiglu: bool
     return (Cc, sC) if swiglu else Cc
 
 
+@_on_tensor_device
 def gemm_fp8(A, sA, B, sB):
     """Dense block-scaled FP8 GEMM: A [M, K] e4m3 + sA, B [N, K] e4m3 codes packed by
     moe_pack_weight_fp8 + sB -> bf16 [M, N]."""
@@ -298,6 +335,7 @@ def gemm_fp8(A, sA, B, sB):
     return Cc
 
 
+@_on_tensor_device
 def grouped_gemm_w4a16(A, B, s7, offsets, R_cap: int, N: int, swiglu: bool = False,
                        a_rows: Optional[torch.Tensor] = None, a_row_div: int = 1):
     K = A.shape[1]
@@ -311,6 +349,7 @@ def grouped_gemm_w4a16(A, B, s7, offsets, R_cap: int, N: int, swiglu: bool = Fal
     return Cc
 
 
+@_on_tensor_device
 def grouped_gemm_f32(A, B, offsets, R_cap: int, N: int, swiglu: bool = False,
                      a_rows: Optional[torch.Tensor] = None, a_row_div: int = 1):
     K = A.shape[1]
@@ -324,6 +363,7 @@ def grouped_gemm_f32(A, B, offsets, R_cap: int, N: int, swiglu: bool = False,
     return Cc
 
 
+@_on_tensor_device
 def moe_combine(o: torch.Tensor, row_of_slot: torch.Tensor, topk_w: torch.Tensor, T: int, k: int,
                 out_dtype=torch.bfloat16):
     d = o.shape[1]
@@ -358,6 +398,7 @@ def moe_layer_workspace_size(desc: LayerDesc) -> int:
     return n
 
 
+@_on_tensor_device
 def moe_layer_fwd(desc: LayerDesc, weights: dict, x: torch.Tensor,
                   token_ids: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   y: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None):
@@ -388,6 +429,7 @@ def moe_layer_chunked_workspace_size(desc: LayerDesc, chunk_tokens: int) -> int:
     return n
 
 
+@_on_tensor_device
 def moe_layer_fwd_chunked(desc: LayerDesc, weights: dict, x: torch.Tensor, chunk_tokens: int,
                           token_ids: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None,

@@ -28,6 +28,8 @@
  *     bitwise identical outputs: no floating-point atomics are used.
  *   - Calls on different streams may run concurrently; calls on one stream are
  *     ordered by the stream.
+ *   - A call checks and launches on the current HIP device: `stream` and every
+ *     pointer must belong to that device.
  */
 #ifndef FP8GG_MOE_H
 #define FP8GG_MOE_H

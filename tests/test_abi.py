@@ -236,3 +236,19 @@ x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resou
 x.hip:9:1: remark: Function Name: _Zbad [-Rpass-analysis=kernel-resource-usage]
 x.hip:9:1: remark:     ScratchSize [bytes/lane]: 44 [-Rpass-analysis=kernel-resource-usage]"""
     assert scratch_users(remarks) == ["_Zbad (44 bytes/lane)"]
+
+
+def test_binding_runs_each_call_on_its_tensors_device():
+    """Every binding call that takes tensors is wrapped so that it runs with the tensors'
+    GPU current (the library launches on the current device); CPU tensors reach the
+    call itself, which refuses them before anything is launched."""
+    import torch
+    import fp8_grouped_gemm_amd as M
+    tensor_calls = [n for n in M.__all__ if n not in (
+        "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route_workspace_size",
+        "moe_layer_workspace_size", "moe_layer_chunked_workspace_size", "MoeError", "LayerDesc")]
+    for name in tensor_calls:
+        assert hasattr(getattr(M, name), "__wrapped__"), name
+    with pytest.raises(ValueError, match="on the GPU"):
+        M.moe_combine(torch.zeros(4, 128), torch.zeros(4, dtype=torch.int32),
+                      torch.zeros(4), 4, 1)
