@@ -552,11 +552,16 @@ int layer_check(const moe_layer_desc* d) {
   if (d->mode == MOE_MODE_FP32) REQUIRE(d->I % 16 == 0, "moe_layer: fp32 needs I %% 16 == 0");
   REQUIRE((long long)d->T * d->k + (long long)d->E * (d->m_align - 1) < (1LL << 31),
           "moe_layer: rows bound overflows int32");
+  // a positive factor whose capacity floor(ceil(T*k/E) * factor) comes out 0 would drop
+  // every slot; the dispatch reads capacity 0 as dropless, so such a factor is refused
+  if (d->capacity_factor > 0 && d->T > 0)
+    REQUIRE(moe_capacity(d->T, d->k, d->E, d->capacity_factor) >= 1,
+            "moe_layer: capacity_factor %g gives capacity floor(ceil(T*k/E) * factor) = 0 "
+            "(use a larger factor, or <= 0 for dropless)", d->capacity_factor);
   if (d->layout == MOE_LAYOUT_MASKED) {
     REQUIRE(d->mode == MOE_MODE_FP8, "moe_layer: the masked layout needs MOE_MODE_FP8");
+    REQUIRE(d->capacity_factor > 0, "moe_layer: the masked layout needs capacity_factor > 0");
     const int cap = moe_capacity(d->T, d->k, d->E, d->capacity_factor);
-    REQUIRE(cap >= 1, "moe_layer: the masked layout needs capacity_factor > 0 "
-                      "(capacity floor(ceil(T*k/E) * factor) >= 1)");
     REQUIRE((long long)d->E * cap * std::max(d->d, d->I) <= kMaxOperandBytes,
             "moe_layer: E * capacity rows exceed the 32-bit operand offset range");
   }

@@ -309,7 +309,8 @@ typedef struct {
   int mode;                /* MOE_MODE_*                                            */
   int route;               /* MOE_ROUTE_SCORE or MOE_ROUTE_HASH (k must be 1)       */
   unsigned route_flags;    /* MOE_ROUTE_RENORM                                      */
-  double capacity_factor;  /* <= 0: dropless                                        */
+  double capacity_factor;  /* <= 0: dropless; > 0: capacity C = moe_capacity(T, k,  */
+                           /* E, capacity_factor), which must be >= 1 when T > 0    */
   int m_align;             /* row padding quantum of each expert (1..1024)          */
   int layout;              /* MOE_LAYOUT_CONTIGUOUS, or MOE_LAYOUT_MASKED (FP8 mode  */
                            /* with capacity_factor > 0: buffers [E, C, *], C =      */

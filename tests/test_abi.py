@@ -204,6 +204,16 @@ def test_masked_dispatch_and_layout_checks():
     bad = D(128, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 2.0, 16, 7)
     assert lib.moe_layer_workspace_size(C.byref(bad)) == 0
     assert "layout" in lib.moe_last_error().decode()
+    # a positive factor whose capacity floors to 0 (ceil(4*2/256) * 0.5 = 0) is refused in
+    # both layouts rather than read as dropless; with no tokens it is harmless
+    for layout in (_lib.MOE_LAYOUT_CONTIGUOUS, _lib.MOE_LAYOUT_MASKED):
+        tiny = D(4, 7168, 256, 2, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.5, 16,
+                 layout)
+        assert lib.moe_layer_workspace_size(C.byref(tiny)) == 0
+        assert "capacity_factor" in lib.moe_last_error().decode()
+        empty = D(0, 7168, 256, 2, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.5, 16,
+                  layout)
+        assert lib.moe_layer_workspace_size(C.byref(empty)) > 0
 
 
 def test_chunked_pipeline_checks():
