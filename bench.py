@@ -249,7 +249,7 @@ def main(argv=None):
                          "--output-format csv run written to DIR, then exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print HBM bytes per dispatch of the GEMM kernels from a FETCH_SIZE "
-                         "and a WRITE_SIZE rocprofv3 --pmc run of --workload (prefill_fp8 or "
+                         "and a WRITE_SIZE rocprofv3 --pmc run of --workload (prefill_fp8, decode_fp8 or "
                          "grouped_gemm_fp8), calibrated on the weight quantiser, then exit")
     a = ap.parse_args(argv)
     if a.trace_summary:
@@ -345,7 +345,8 @@ def main(argv=None):
         log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
     g1_ms = stages.get("gemm1")
     roofline = None
-    traffic = measured_traffic("gemm1") if a.workload == "prefill_fp8" else None
+    traffic = (measured_traffic("gemm1", TRAFFIC_FILES[a.workload])
+               if a.workload in ("prefill_fp8", "decode_fp8") and not masked else None)
     if g1_ms and w.mode == "w4a16":
         # int4 weights streamed once against T rows: ~430 FLOP/B, above the bf16 ridge
         # (2500 TFLOP/s / 8 TB/s = 312 FLOP/B), so the bound is the bf16 MFMA peak
@@ -482,7 +483,12 @@ def pmc_summary(dirname):
 # calibration kernel of the traffic counters (reads 4 B and writes 1 B per element, plus
 # one fp32 scale per 128 x 128 block)
 CALIB_WEIGHTS = {"prefill_fp8": [(256, 4096, 7168), (256, 7168, 2048)],
+                 "decode_fp8": [(256, 4096, 7168), (256, 7168, 2048)],
                  "grouped_gemm_fp8": [(16, 4096, 7168)]}
+# committed traffic summary of each workload (profiles/)
+TRAFFIC_FILES = {"prefill_fp8": "gemm_fp8_prefill_traffic.json",
+                 "decode_fp8": "gemm_fp8_decode_traffic.json",
+                 "grouped_gemm_fp8": "grouped_gemm_fp8_traffic.json"}
 CALIB_KERNEL = "moe::quant_weight_fp8_kernel"
 
 
@@ -512,7 +518,7 @@ def traffic_summary(fetch_dir, write_dir, workload):
     # roles: the layer's GEMM1 (SwiGLU epilogue) and GEMM2, or the standalone GEMM
     roles = {}
     for k, v in out["kernels"].items():
-        if workload == "prefill_fp8" and "gemm_fp8_kernel" in k:
+        if workload in ("prefill_fp8", "decode_fp8") and "gemm_fp8_kernel" in k:
             roles["gemm1" if ", true" in k else "gemm2"] = dict(v, kernel=k)
         elif workload == "grouped_gemm_fp8" and "gemm_fp8_kernel" in k:
             roles["gemm"] = dict(v, kernel=k)
@@ -565,7 +571,7 @@ def bench_grouped_gemm(M, steps, warmup, settle_s=SETTLE_S):
                                    "128), N=4096, K=7168, bf16 out", "group_sizes": sizes.tolist()},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
-                         "traffic": measured_traffic("gemm", "grouped_gemm_fp8_traffic.json"),
+                         "traffic": measured_traffic("gemm", TRAFFIC_FILES["grouped_gemm_fp8"]),
                          "algorithmic_bytes": int(R * K + R * (K // 128) * 4 + 16 * N * K
                                                   + 16 * (N // 128) * (K // 128) * 4
                                                   + R * N * 2)}}
