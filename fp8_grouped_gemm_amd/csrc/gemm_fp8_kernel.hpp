@@ -343,8 +343,17 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
           s7q[slot][j] =
               *reinterpret_cast<const v4f*>(s7_base + (size_t)j * s7_next + (size_t)kb * 16);
         } else {
-          const v4i lo = *reinterpret_cast<const v4i*>(p + b_lane);
-          const v4i hi = *reinterpret_cast<const v4i*>(p + 1024 + b_lane);
+          // small SwiGLU tiles (the layer's up/gate projection for light experts: pure
+          // weight streams over K = d) load non-temporally, which measured 6-8% faster
+          // there; in the plain instance (the down projection, K = I) it was slower
+          v4i lo, hi;
+          if constexpr (BM <= 32 && SWIGLU) {
+            lo = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p + b_lane));
+            hi = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p + 1024 + b_lane));
+          } else {
+            lo = *reinterpret_cast<const v4i*>(p + b_lane);
+            hi = *reinterpret_cast<const v4i*>(p + 1024 + b_lane);
+          }
           bq[slot][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
       }
