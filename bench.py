@@ -224,6 +224,56 @@ def settle(fn, seconds):
     torch.cuda.synchronize()
 
 
+def measured_peaks(M, reps=5):
+    """The rates this GPU reaches, from the library's two probes, timed with HIP events
+    on the launch stream: the FP8 matrix core (16x16x128 e4m3 MFMAs, two waves per SIMD
+    on every CU) and HBM reads (a 4 GiB buffer read once per call with 16-byte
+    non-temporal loads; the better of one and sixteen 512-thread workgroups per CU, the
+    two grid shapes that read fastest in a sweep of 1-16).  References beside the
+    datasheet peaks."""
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 50000
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(lambda: M.moe_probe_mfma_fp8(cus, iters))
+    mfma = cus * 8 * iters * 4 * 65536 / (ms * 1e-3) / 1e12
+    buf = torch.randint(-2**31, 2**31 - 1, (1 << 30,), dtype=torch.int32, device=dev)
+    ms_r = min(timed(lambda: M.moe_probe_hbm_read(buf, m * cus)) for m in (1, 16))
+    del buf
+    return {"mfma_fp8_tflops": round(mfma, 1),
+            "hbm_read_gbs": round((4 << 30) / (ms_r * 1e-3) / 1e9, 1),
+            "probes": f"FP8 MFMA loop ({cus} workgroups x 8 waves x {iters} x 4 16x16x128 "
+                      f"MFMAs) and a 4 GiB non-temporal read (best of {cus} and {16 * cus} "
+                      f"workgroups), {reps} timed calls each"}
+
+
+def with_measured(roofline, peaks):
+    """Add the measured peak of the roofline's bound (FP8 MFMA or HBM read) and the
+    fraction of it achieved."""
+    if not roofline or not peaks:
+        return roofline
+    if roofline["bound"] == "hbm":
+        mp = peaks["hbm_read_gbs"]
+    elif roofline["bound"] == "mfma" and roofline["peak"] == PEAK_FP8_TFLOPS:
+        mp = peaks["mfma_fp8_tflops"]
+    else:
+        return roofline
+    roofline["measured_peak"] = mp
+    roofline["frac_of_measured"] = round(roofline["achieved"] / mp, 4)
+    return roofline
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +291,8 @@ def main(argv=None):
                          "chunks of this many tokens instead of the single pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--no-measured-peak", action="store_true",
+                    help="skip the MFMA and HBM probes that give the measured peaks")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print a per-kernel summary of a rocprofv3 --kernel-trace --stats "
                          "--output-format csv run written to DIR, then exit")
@@ -267,14 +319,14 @@ def main(argv=None):
         return 2
 
     import fp8_grouped_gemm_amd as M
-    if a.workload == "grouped_gemm_fp8":
-        print(json.dumps(bench_grouped_gemm(M, a.steps, a.warmup, a.settle)), flush=True)
-        return 0
-    if a.workload == "dense_gemm_fp8":
-        print(json.dumps(bench_dense_gemm(M, a.steps, a.warmup, a.settle)), flush=True)
-        return 0
-    if a.workload == "masked_gemm_fp8":
-        print(json.dumps(bench_masked_gemm(M, a.steps, a.warmup, a.settle)), flush=True)
+    gemm_benches = {"grouped_gemm_fp8": bench_grouped_gemm, "dense_gemm_fp8": bench_dense_gemm,
+                    "masked_gemm_fp8": bench_masked_gemm}
+    if a.workload in gemm_benches:
+        res = gemm_benches[a.workload](M, a.steps, a.warmup, a.settle)
+        if not a.no_measured_peak:
+            res["measured_peak"] = measured_peaks(M)
+            with_measured(res.get("roofline"), res["measured_peak"])
+        print(json.dumps(res), flush=True)
         return 0
     # the decode layer in the fixed-capacity layout: C = ceil(T k / E) * 2
     masked = a.workload == "decode_fp8_masked"
@@ -407,6 +459,9 @@ def main(argv=None):
         "stages_ms": {k: round(v, 4) for k, v in stages.items()} or None,
         "roofline": roofline,
     }
+    if not a.no_measured_peak:
+        out["measured_peak"] = measured_peaks(M)
+        with_measured(roofline, out["measured_peak"])
     if (not a.no_cpu_baseline and w.mode == "fp8" and w.route == "score" and not masked
             and not a.chunk_tokens):
         log("timing the CPU oracle on a bounded sample")

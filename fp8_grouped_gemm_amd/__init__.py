@@ -27,7 +27,7 @@ __all__ = [
     "gemm_fp8", "grouped_gemm_w4a16",
     "grouped_gemm_f32", "moe_combine", "moe_layer_workspace_size", "moe_layer_fwd", "MoeError",
     "moe_layer_chunked_workspace_size", "moe_layer_fwd_chunked",
-    "LayerDesc",
+    "LayerDesc", "moe_probe_mfma_fp8", "moe_probe_hbm_read",
 ]
 
 
@@ -372,6 +372,33 @@ def moe_combine(o: torch.Tensor, row_of_slot: torch.Tensor, topk_w: torch.Tensor
     _lib.check(_lib_().moe_combine(_ptr(o), _dt(o), _ptr(row_of_slot), _ptr(topk_w), T, k, d,
                                    _ptr(y), _dt(y), _stream(dev)), "moe_combine")
     return y
+
+
+# --------------------------------------------------------- measurement probes
+
+def moe_probe_mfma_fp8(n_blocks: int, iters: int, code: int = 0x38,
+                       device: Optional[torch.device] = None):
+    """Enqueue the FP8 matrix-core probe on the current stream of `device` (default
+    cuda:0); returns its fp32 output [n_blocks * 512] (n_blocks * 8 * iters * 4 * 65536
+    FLOP are performed)."""
+    dev = torch.device(device or "cuda:0")
+    out = torch.empty(n_blocks * 512, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib_().moe_probe_mfma_fp8(n_blocks, iters, code, _ptr(out), _stream(dev)),
+                   "moe_probe_mfma_fp8")
+    return out
+
+
+@_on_tensor_device
+def moe_probe_hbm_read(buf: torch.Tensor, n_blocks: int):
+    """Enqueue the HBM read probe over the bytes of `buf`; returns the per-workgroup
+    XORs of the 32-bit words read (uint32 stored as int32) [n_blocks]."""
+    dev = buf.device
+    out = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * buf.element_size()
+    _lib.check(_lib_().moe_probe_hbm_read(_ptr(buf), nbytes, n_blocks, _ptr(out), _stream(dev)),
+               "moe_probe_hbm_read")
+    return out
 
 
 # ---------------------------------------------------------------------- layer

@@ -69,6 +69,8 @@ SIGNATURES = {
     "moe_layer_workspace_size": (_Z, [C.POINTER(MoeLayerDesc)]),
     "moe_layer_fwd": (_I, [C.POINTER(MoeLayerDesc), C.POINTER(MoeLayerWeights), _P, _P, _P, _P,
                            _Z, _P, _P]),
+    "moe_probe_mfma_fp8": (_I, [_I, _I, C.c_uint8, _P, _P]),
+    "moe_probe_hbm_read": (_I, [_P, _Z, _I, _P, _P]),
     "moe_layer_chunked_workspace_size": (_Z, [C.POINTER(MoeLayerDesc), _I]),
     "moe_layer_fwd_chunked": (_I, [C.POINTER(MoeLayerDesc), C.POINTER(MoeLayerWeights), _P, _P,
                                    _P, _P, _Z, _I, _P, _P]),

@@ -512,6 +512,29 @@ int moe_combine(const void* o, moe_dtype o_dt, const int32_t* row_of_slot, const
                     "combine launch");
 }
 
+// ------------------------------------------------------------ measurement probes
+int moe_probe_mfma_fp8(int n_blocks, int iters, uint8_t code, float* out, void* stream) {
+  REQUIRE(out, "moe_probe_mfma_fp8: null pointer");
+  REQUIRE(n_blocks >= 1 && n_blocks <= 65536, "moe_probe_mfma_fp8: n_blocks must be in [1, 65536]");
+  REQUIRE(iters >= 1, "moe_probe_mfma_fp8: iters must be positive");
+  REQUIRE((code & 0x7F) != 0x7F, "moe_probe_mfma_fp8: code 0x%02x is a NaN", code);
+  int st = current_device(nullptr);
+  if (st) return st;
+  return hip_status(moe::launch_probe_mfma_fp8(n_blocks, iters, code, out, S(stream)),
+                    "mfma probe launch");
+}
+
+int moe_probe_hbm_read(const void* buf, size_t bytes, int n_blocks, uint32_t* out,
+                       void* stream) {
+  REQUIRE(buf && out, "moe_probe_hbm_read: null pointer");
+  REQUIRE(bytes >= 16 && bytes % 16 == 0, "moe_probe_hbm_read: bytes must be a positive multiple of 16");
+  REQUIRE(n_blocks >= 1 && n_blocks <= 65536, "moe_probe_hbm_read: n_blocks must be in [1, 65536]");
+  int st = current_device(nullptr);
+  if (st) return st;
+  return hip_status(moe::launch_probe_read(buf, bytes, n_blocks, out, S(stream)),
+                    "read probe launch");
+}
+
 // ------------------------------------------------------------------- layer
 namespace {
 

@@ -69,6 +69,11 @@ hipError_t launch_gemm_w4a16(const uint16_t* A, const int32_t* a_rows, int a_row
 hipError_t launch_gemm_f32(const float* A, const int32_t* a_rows, int a_row_div, const float* B,
                            const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
                            float* C, hipStream_t s);
+// measurement probes (probe.hip): n_blocks workgroups of 512 threads each
+hipError_t launch_probe_mfma_fp8(int n_blocks, int iters, uint32_t code, float* out,
+                                 hipStream_t s);
+hipError_t launch_probe_read(const void* buf, size_t bytes, int n_blocks, uint32_t* out,
+                             hipStream_t s);
 hipError_t launch_combine(const void* o, bool o_bf16, const int32_t* row_of_slot,
                           const float* w, int T, int k, int d, void* y, bool y_bf16,
                           hipStream_t s);

@@ -374,6 +374,29 @@ int moe_layer_fwd_chunked(const moe_layer_desc *desc, const moe_layer_weights *w
                           const int64_t *token_ids, void *y, void *ws, size_t ws_bytes,
                           int chunk_tokens, void *stream, void *stream_aux);
 
+/* ---- measurement probes (not part of the layer's computation) ----
+ * References for the rooflines the layer's kernels are measured against: the rates the
+ * FP8 matrix core and the HBM read path reach on this device, beside the datasheet
+ * peaks.  Both enqueue one kernel of n_blocks workgroups of 512 threads on `stream`;
+ * the caller times it (HIP events on `stream`). */
+
+/* FP8 matrix-core issue rate.  Every wave runs `iters` rounds of four independent
+ * 16x16x128 e4m3 MFMAs (the FP8 GEMMs' instruction) on operands whose bytes all equal
+ * `code` (an e4m3 code, not a NaN), so the call performs n_blocks * 8 * iters * 4 *
+ * 65536 FLOP.  out: device fp32 [n_blocks * 512], fully written; lane i's value is
+ * 2048 * iters * v^2 for the code's value v (exact while 128 * iters * v^2 < 2^24).
+ * n_blocks in [1, 65536] (one per CU runs two waves per SIMD, as the GEMMs do),
+ * iters >= 1. */
+int moe_probe_mfma_fp8(int n_blocks, int iters, uint8_t code, float *out, void *stream);
+
+/* HBM read rate.  Reads the `bytes` bytes at `buf` (device, 16-byte aligned, bytes a
+ * positive multiple of 16) once with 16-byte non-temporal loads, grid-strided over
+ * n_blocks workgroups (n_blocks in [1, 65536]); out: device uint32 [n_blocks], fully
+ * written, the XOR of the 32-bit words that workgroup read (so the XOR over out is the
+ * XOR of the whole buffer). */
+int moe_probe_hbm_read(const void *buf, size_t bytes, int n_blocks, uint32_t *out,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

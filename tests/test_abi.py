@@ -23,7 +23,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = _lib.load()
     declared = _declared()
-    assert len(declared) == 27, declared
+    assert len(declared) == 29, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -256,9 +256,24 @@ def test_binding_runs_each_call_on_its_tensors_device():
     import fp8_grouped_gemm_amd as M
     tensor_calls = [n for n in M.__all__ if n not in (
         "moe_device_supported", "moe_capacity", "moe_rows_bound", "moe_route_workspace_size",
-        "moe_layer_workspace_size", "moe_layer_chunked_workspace_size", "MoeError", "LayerDesc")]
+        "moe_layer_workspace_size", "moe_layer_chunked_workspace_size", "MoeError", "LayerDesc",
+        "moe_probe_mfma_fp8")]   # (takes a device, not tensors, and makes it current itself)
     for name in tensor_calls:
         assert hasattr(getattr(M, name), "__wrapped__"), name
     with pytest.raises(ValueError, match="on the GPU"):
         M.moe_combine(torch.zeros(4, 128), torch.zeros(4, dtype=torch.int32),
                       torch.zeros(4), 4, 1)
+
+
+def test_probes_reject_bad_args():
+    lib = _lib.load()
+    S = None
+    _err(lib.moe_probe_mfma_fp8(4, 10, 0x38, None, S), "null")
+    _err(lib.moe_probe_mfma_fp8(0, 10, 0x38, FAKE, S), "n_blocks")
+    _err(lib.moe_probe_mfma_fp8(4, 0, 0x38, FAKE, S), "iters")
+    _err(lib.moe_probe_mfma_fp8(4, 10, 0x7F, FAKE, S), "NaN")
+    _err(lib.moe_probe_mfma_fp8(4, 10, 0xFF, FAKE, S), "NaN")
+    _err(lib.moe_probe_hbm_read(None, 1024, 4, FAKE, S), "null")
+    _err(lib.moe_probe_hbm_read(FAKE, 1000, 4, FAKE, S), "multiple of 16")
+    _err(lib.moe_probe_hbm_read(FAKE, 0, 4, FAKE, S), "multiple of 16")
+    _err(lib.moe_probe_hbm_read(FAKE, 1024, 0, FAKE, S), "n_blocks")
