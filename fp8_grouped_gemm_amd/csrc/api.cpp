@@ -672,13 +672,13 @@ int layer_args(const char* fn, const moe_layer_desc* d, const moe_layer_weights*
                const int64_t* token_ids, const void* y, const void* ws) {
   int st = layer_check(d);
   if (st) return st;
-  REQUIRE(w && x && y && ws, "%s: null pointer", fn);
+  REQUIRE(w && ws && ((x && y) || d->T == 0), "%s: null pointer", fn);  // (T = 0: x, y empty)
   REQUIRE(w->w13 && w->w2, "%s: null expert weights", fn);
   if (d->mode != MOE_MODE_FP32) REQUIRE(w->s13 && w->s2, "%s: null weight scales", fn);
   if (d->route == MOE_ROUTE_SCORE)
     REQUIRE(w->w_router && w->bias, "%s: score routing needs w_router and bias", fn);
   else
-    REQUIRE(token_ids, "%s: hash routing needs token_ids", fn);
+    REQUIRE(token_ids || d->T == 0, "%s: hash routing needs token_ids", fn);
   return MOE_OK;
 }
 
@@ -799,7 +799,12 @@ int moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* w, const voi
   const LayerWs L = layer_ws(d);
   if (ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_layer_fwd: workspace %zu < %zu bytes", ws_bytes, L.total);
-  if (d->T == 0) return MOE_OK;
+  if (d->T == 0) {
+    // no tokens: y is empty and every expert's routed count is 0
+    if (!counts_out) return MOE_OK;
+    if ((st = current_device(nullptr))) return st;
+    return hip_status(moe::launch_fill_i32(counts_out, d->E, 0, S(stream)), "fill launch");
+  }
   int cus = 0;
   if ((st = current_device(&cus))) return st;
   const LayerPtrs P = layer_ptrs(static_cast<uint8_t*>(ws), L, counts_out);

@@ -214,4 +214,17 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int m_align,
   return hipGetLastError();
 }
 
+// n int32 values set to v (a kernel rather than a memset node, so that a captured graph
+// replays it like the other kernels)
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int n, int v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
 }  // namespace moe

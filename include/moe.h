@@ -340,10 +340,11 @@ size_t moe_layer_workspace_size(const moe_layer_desc *desc);
  * of G(x)_i E_i(x) with E_i a SwiGLU FFN (MegaMoE walkthrough, discosf.com, sec.
  * 2.1-2.2 and 3.2-3.3; hash routing and 4-bit weights, DeepSeek-V4 lecture, tqpw.cn,
  * sec. 2.2 and 3.1; capacity drop, DeepSeek MoE architecture, mooersco.com, sec. 2.5).
- *   x [T, d]: fp32 (FP32 mode) or bf16; token_ids [T] int64 for hash routing;
+ *   x [T, d]: fp32 (FP32 mode) or bf16; token_ids [T] int64 for hash routing (x, y and
+ *   token_ids may be NULL when T = 0);
  *   y [T, d] output: fp32 (FP32 mode) or bf16;
  *   ws / ws_bytes: caller-owned device workspace (>= moe_layer_workspace_size);
- *   counts_out [E] int32 (may be NULL): routed slots per expert.
+ *   counts_out [E] int32 (may be NULL): routed slots per expert (all 0 when T = 0).
  * Contiguous layout: GEMM1 reads activation rows through the dispatch map, so no
  * gathered copy of the activations is made.  Masked layout: moe_dispatch_masked, the
  * token codes gathered into the [E, C, d] buffer (1x128 quantisation, empty rows zero),

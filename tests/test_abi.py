@@ -145,6 +145,15 @@ def test_layer_descriptor_checks_and_workspace():
     w = _lib.MoeLayerWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE)
     st = lib.moe_layer_fwd(C.byref(good), C.byref(w), FAKE, None, FAKE, FAKE, n, None, None)
     assert st == _lib.MOE_ERR_INVALID_ARG
+    # no tokens: x, y (and token_ids) may be null; with no counts to report nothing runs
+    w = _lib.MoeLayerWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    empty = D(0, 7168, 256, 8, 2048, _lib.MOE_MODE_FP8, _lib.MOE_ROUTE_SCORE, 0, 0.0, 128)
+    n0 = lib.moe_layer_workspace_size(C.byref(empty))
+    assert n0 > 0
+    assert lib.moe_layer_fwd(C.byref(empty), C.byref(w), None, None, None, FAKE, n0, None,
+                             None) == _lib.MOE_OK
+    _err(lib.moe_layer_fwd(C.byref(good), C.byref(w), None, None, FAKE, FAKE, n, None, None),
+         "null")
 
 
 def test_binding_refuses_missing_library(monkeypatch, tmp_path):

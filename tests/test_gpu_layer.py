@@ -154,6 +154,32 @@ def test_layer_big_tiles(monkeypatch):
     run_layer_case(w, tokens=[0, 1, 2, 100, 511, 512, 700, 1000, 1022, 1023])
 
 
+@pytest.mark.parametrize("mode", ["fp8", "fp32", "w4a16"])
+def test_layer_single_token(mode):
+    """Degenerate batch: one token, every one of its k experts holding a single row (the
+    rest empty), k = E - 1 so that one expert is untouched."""
+    route = "hash" if mode == "w4a16" else "score"
+    run_layer_case(synth.Workload(f"one_{mode}", T=1, d=256, E=8, k=1 if route == "hash" else 7,
+                                  I=256, mode=mode, route=route, m_align=16, seed=4))
+
+
+@pytest.mark.parametrize("mode", ["fp8", "fp32"])
+def test_layer_no_tokens(mode):
+    """T = 0: nothing to compute, and the reported routed counts are all 0 (the output
+    buffer is overwritten, whatever it held)."""
+    note(f"layer T=0 mode={mode}")
+    w = synth.Workload(f"empty_{mode}", T=4, d=256, E=8, k=2, I=256, mode=mode, m_align=16)
+    inp = synth.layer_inputs(w)
+    gw = _gpu_weights(w, inp)
+    desc = M.LayerDesc(0, w.d, w.E, w.k, w.I, mode=w.mode, route=w.route, m_align=w.m_align)
+    x = inp["x"][:0].to(dev())
+    counts = torch.full((w.E,), -7, dtype=torch.int32, device=dev())
+    y, counts = M.moe_layer_fwd(desc, gw, x, None, counts=counts)
+    torch.cuda.synchronize()
+    assert y.shape == (0, w.d)
+    assert torch.equal(counts.cpu(), torch.zeros(w.E, dtype=torch.int32))
+
+
 def test_layer_small_fp8_many_experts():
     run_layer_case(synth.Workload("small_fp8_e64", T=200, d=384, E=64, k=6, I=128, mode="fp8",
                                   m_align=32, seed=3))
