@@ -20,7 +20,11 @@ __device__ __forceinline__ void add_rows(const void* __restrict__ o, const int* 
   for (int u = 0; u < KU; ++u) {                  // slots past n or dropped read row 0
     const size_t r = (size_t)max(u < n ? rows[u] : 0, 0);
     if (OBF16) {
-      raw[u][0] = *reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(o) + r * d + c * 8);
+      const v4i* p = reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(o) + r * d + c * 8);
+      // each o row is read once: with four or more rows per token the loads are
+      // non-temporal (prefill, k = 8: 108 -> 96 us; with one row per token they measured
+      // slower, 21 -> 24 us)
+      raw[u][0] = KU >= 4 ? __builtin_nontemporal_load(p) : *p;
     } else {
       const float* p = static_cast<const float*>(o) + r * d + c * 8;
       raw[u][0] = *reinterpret_cast<const v4i*>(p);
