@@ -114,28 +114,31 @@ __device__ __forceinline__ v8i expand_int4_e4m3(v4i w) {
 // W4: the weights are 4-bit codes in [-7, 7] with one fp32 scale per output channel and
 // 128-deep K block (expand_int4_e4m3 below), whose scales, packed [G][R/16][K/128][16],
 // the kernel reads through args.wsc.  Otherwise e4m3 codes with 128x128 block scales sB.
-template <int BMS, bool SWIGLU, bool W4 = false>
+template <int BMS, bool SWIGLU, bool W4 = false, int BMB = 128>
 __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
                                                            const float* __restrict__ sB) {
-  constexpr int NW = 8, NT = 512, BMB = 128, TN = 2;
+  static_assert(BMB == 128 || (BMB == 192 && !W4), "large-tile rows");
+  constexpr int NW = 8, NT = 512, TN = 2;
   constexpr int BN_OUT = SWIGLU ? 128 : 256;       // output columns per tile
   constexpr int WB = (SWIGLU ? 128 : 256) / NW;    // weight rows per wave (per half: SwiGLU)
   constexpr int A_STAGE = BMB * 128;               // activation codes of one K block
   // activation stage arrays (W4: three, so that its weight ring can be two blocks deep;
   // the ring must cover the activation lead)
-  constexpr int NSA = W4 ? 3 : 4;
+  // (192-row tiles: three, for LDS; measured enough at their longer blocks)
+  constexpr int NSA = (W4 || BMB > 128) ? 3 : 4;
   // scale table [kb][row], rows of TS floats: the 4-float pad puts the four 16-row
   // groups one fill instruction writes (four consecutive K-block quads) in different banks
   constexpr int TS = BMB + 4;
-  constexpr int TAB_FLOATS = kGemmMaxKBlocks * TS;
-  constexpr int OUT_FLOATS = BMB * 132;             // epilogue rows of 528 bytes
+  constexpr int TAB_FLOATS = (BMB > 128 ? kGemmMaxKBlocks192 : kGemmMaxKBlocks) * TS;
+  // epilogue rows of 528 bytes (192-row tiles: staged in two passes of 96 rows)
+  constexpr int OUT_FLOATS = (BMB > 128 ? BMB / 2 : BMB) * 132;
   __shared__ TileMap tm;
   // four activation stages, each an LDS object of its own (see dma16b); the row-scale
   // table [kb][row] doubles as the epilogue's staging area
   __shared__ __attribute__((aligned(1024))) uint8_t st0[A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[A_STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[W4 ? 16 : A_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[NSA == 4 ? A_STAGE : 16];
   __shared__ __attribute__((aligned(1024))) float tab[TAB_FLOATS > OUT_FLOATS ? TAB_FLOATS : OUT_FLOATS];
   __shared__ int row_src[BMB];
   // product tables: the tile's two weight-scale rows, table t at [t * PT_KB + kb]
@@ -186,7 +189,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     // weight ring: blocks kb .. kb+DB-1.  Small tiles only stream weights, so they keep
     // more blocks in flight (their accumulators are few).
     // (W4: half the bytes per block and a larger register set per block, so fewer)
-    constexpr int DB = BM <= 32 ? (W4 ? 4 : 6) : (W4 ? 2 : 3);
+    // (192-row tiles: two, for registers)
+    constexpr int DB = BM <= 32 ? (W4 ? 4 : 6) : ((W4 || BM > 128) ? 2 : 3);
     constexpr int LEAD = NSA - 1;                  // activation DMA runs LEAD blocks ahead
     static_assert(LEAD <= DB, "prologue order");
     // the K loop is unrolled by UNR blocks, so that weight slots and activation stages
@@ -212,9 +216,13 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       // half last tile, whose second-half waves use the first table)
       const int cb0 = n0 / 128;
       const int cb1 = SWIGLU ? (N + n0) / 128 : min(cb0 + 1, RB - 1);
-      if (tid < 2 * PT_KB) {
-        const int t = tid / PT_KB, kb = tid - t * PT_KB;
-        if (kb < KB) sbt[tid] = sB[((size_t)g * RB + (t ? cb1 : cb0)) * KB + kb];
+      // (192-row tiles: the thread index made opaque here, so that these addresses are
+      // formed per tile instead of being hoisted out of the tile loop into registers)
+      int tq = tid;
+      if constexpr (BMB > 128) asm volatile("" : "+v"(tq));
+      if (tq < 2 * PT_KB) {
+        const int t = tq / PT_KB, kb = tq - t * PT_KB;
+        if (kb < KB) sbt[tq] = sB[((size_t)g * RB + (t ? cb1 : cb0)) * KB + kb];
       }
     }
     __syncthreads();
@@ -379,8 +387,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     // PROD: a step's promotion reads its scale set straight from the ring (SR sets, one
     // more than the fragments, so the set is still there one step later); otherwise
     // the scale products are formed in the step (cq).
-    constexpr int RA = TM < 2 ? TM : 2;
-    constexpr int AR = 3;                          // divides UNR * TM
+    // (192-row tiles: one step ahead, a ring of two, for registers)
+    constexpr int RA = TM < 2 ? TM : (TM > 8 ? 1 : 2);
+    constexpr int AR = (RA == 1 && TM > 8) ? 2 : 3;  // divides UNR * TM
     constexpr int SR = (PROD || W4) ? RA + 2 : AR;
     constexpr int PR = (TM % 2 == 0) ? 2 : 3;      // divides UNR * TM
     constexpr int NSC = (PROD && SWIGLU) ? 2 : 1;  // scale sets per step
@@ -616,90 +625,107 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
       // bf16 tile staged through LDS for 16-byte stores; rows of 528 bytes put the 16
       // rows of one 8-byte write in different banks
       constexpr int OB = 528;
+      // passes of RP rows (192-row tiles: two, so the staging fits the table's LDS)
+      constexpr int NPASS = BM > 128 ? 2 : 1, RP = BM / NPASS, TMP = TM / NPASS;
       uint8_t* ot = reinterpret_cast<uint8_t*>(tab);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int trow = i * 16 + (lane & 15);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int tcol = wid * WB + j * 16 + (lane >> 4) * 4;
-          const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][0]) |
-                              ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][j][2]) |
-                              ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
-          *reinterpret_cast<uint2*>(ot + trow * OB + tcol * 2) = make_uint2(lo, hi);
-        }
-      }
-      __syncthreads();
       uint8_t* C = static_cast<uint8_t*>(args.C);
-      if (ncols == BN_OUT) {
-        // full tile: thread tid takes 16-byte chunk tid % 32 of rows tid / 32 + 16 k; all
-        // LDS reads go out before the stores
-        constexpr int CPR = BN_OUT * 2 / 16, RPP = NT / CPR;
-        static_assert(BM % RPP == 0, "store passes");
-        const int ch = tid % CPR, tr0 = tid / CPR;
-        v4i ov[BM / RPP];
 #pragma unroll
-        for (int k = 0; k < BM / RPP; ++k)
-          ov[k] = *reinterpret_cast<const v4i*>(ot + (tr0 + k * RPP) * OB + ch * 16);
+      for (int ps = 0; ps < NPASS; ++ps) {
 #pragma unroll
-        for (int k = 0; k < BM / RPP; ++k) {
-          const int trow = tr0 + k * RPP;
-          if (trow < n_valid)
-            *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) = ov[k];
+        for (int ii = 0; ii < TMP; ++ii) {
+          const int i = ps * TMP + ii;
+          const int trow = ii * 16 + (lane & 15);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int tcol = wid * WB + j * 16 + (lane >> 4) * 4;
+            const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][0]) |
+                                ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][j][2]) |
+                                ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
+            *reinterpret_cast<uint2*>(ot + trow * OB + tcol * 2) = make_uint2(lo, hi);
+          }
         }
-      } else {
-        const int cpr = ncols * 2 / 16;            // 16-byte chunks per valid row
-        for (int c = tid; c < n_valid * cpr; c += NT) {
-          const int trow = c / cpr, ch = c % cpr;
-          *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) =
-              *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
+        __syncthreads();
+        if (ncols == BN_OUT) {
+          // full tile: thread tid takes 16-byte chunk tid % 32 of rows tid / 32 + 16 k; all
+          // LDS reads go out before the stores
+          constexpr int CPR = BN_OUT * 2 / 16, RPP = NT / CPR;
+          static_assert(RP % RPP == 0, "store passes");
+          const int ch = tid % CPR, tr0 = tid / CPR;
+          v4i ov[RP / RPP];
+#pragma unroll
+          for (int k = 0; k < RP / RPP; ++k)
+            ov[k] = *reinterpret_cast<const v4i*>(ot + (tr0 + k * RPP) * OB + ch * 16);
+#pragma unroll
+          for (int k = 0; k < RP / RPP; ++k) {
+            const int trow = ps * RP + tr0 + k * RPP;
+            if (trow < n_valid)
+              *reinterpret_cast<v4i*>(C + ((size_t)(row0 + trow) * N + n0) * 2 + ch * 16) = ov[k];
+          }
+        } else {
+          const int cpr = ncols * 2 / 16;            // 16-byte chunks per valid row
+          const int nv = min(n_valid - ps * RP, RP);
+          for (int c = tid; c < nv * cpr; c += NT) {
+            const int trow = c / cpr, ch = c % cpr;
+            *reinterpret_cast<v4i*>(C + ((size_t)(row0 + ps * RP + trow) * N + n0) * 2 +
+                                    ch * 16) =
+                *reinterpret_cast<const v4i*>(ot + trow * OB + ch * 16);
+          }
         }
+        if (NPASS > 1) __syncthreads();
       }
     } else {
       // h = silu(gate) * up goes to LDS in fp32 (row stride 132 floats); then four
       // threads per row take the row's 1x128 block: max |h|, the scale, the codes
       constexpr int HS = 132;
+      constexpr int NPASS = BM > 128 ? 2 : 1, RP = BM / NPASS, TMP = TM / NPASS;
       float* hsm = tab;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int trow = i * 16 + (lane & 15);
-        const int tcol = wid * WB + (lane >> 4) * 4;
-        v4f h;
+      for (int ps = 0; ps < NPASS; ++ps) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = silu_fast(acc[i][0][r]) * acc[i][1][r];
-        *reinterpret_cast<v4f*>(hsm + trow * HS + tcol) = h;
-      }
-      __syncthreads();
-      const int row = tid >> 2, part = tid & 3;
-      float hv[32];
-      float m = 0.f;
-      if (row < BM) {
+        for (int ii = 0; ii < TMP; ++ii) {
+          const int i = ps * TMP + ii;
+          const int trow = ii * 16 + (lane & 15);
+          const int tcol = wid * WB + (lane >> 4) * 4;
+          v4f h;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const v4f x = *reinterpret_cast<const v4f*>(hsm + row * HS + part * 32 + q * 4);
+          for (int r = 0; r < 4; ++r) h[r] = silu_fast(acc[i][0][r]) * acc[i][1][r];
+          *reinterpret_cast<v4f*>(hsm + trow * HS + tcol) = h;
+        }
+        __syncthreads();
+        const int row = tid >> 2, part = tid & 3;
+        float hv[32];
+        float m = 0.f;
+        if (row < RP) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hv[q * 4 + e] = x[e];
-            m = fmaxf(m, fabsf(x[e]));
+          for (int q = 0; q < 8; ++q) {
+            const v4f x = *reinterpret_cast<const v4f*>(hsm + row * HS + part * 32 + q * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              hv[q * 4 + e] = x[e];
+              m = fmaxf(m, fabsf(x[e]));
+            }
           }
         }
-      }
-      m = fmaxf(m, __shfl_xor(m, 1, 64));
-      m = fmaxf(m, __shfl_xor(m, 2, 64));
-      if (row < n_valid) {
-        // the activation quantiser's rule: s = fl32(amax / 448), q = e4m3(fl32(h / s)),
-        // with correctly rounded divisions (not a multiply by a rounded reciprocal)
-        const float sc = block_scale(m);
-        uint32_t w[8];
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        const int grow = ps * RP + row;
+        if (row < RP && grow < n_valid) {
+          // the activation quantiser's rule: s = fl32(amax / 448), q = e4m3(fl32(h / s)),
+          // with correctly rounded divisions (not a multiply by a rounded reciprocal)
+          const float sc = block_scale(m);
+          uint32_t w[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          w[q] = e4m3x4(clamp448(hv[4 * q] / sc), clamp448(hv[4 * q + 1] / sc),
-                        clamp448(hv[4 * q + 2] / sc), clamp448(hv[4 * q + 3] / sc));
-        uint8_t* C = static_cast<uint8_t*>(args.C) + (size_t)(row0 + row) * N + n0 + part * 32;
-        *reinterpret_cast<v4i*>(C) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-        *reinterpret_cast<v4i*>(C + 16) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-        if (part == 0) args.sC[(size_t)(row0 + row) * (N / 128) + n0 / 128] = sc;
+          for (int q = 0; q < 8; ++q)
+            w[q] = e4m3x4(clamp448(hv[4 * q] / sc), clamp448(hv[4 * q + 1] / sc),
+                          clamp448(hv[4 * q + 2] / sc), clamp448(hv[4 * q + 3] / sc));
+          uint8_t* C =
+              static_cast<uint8_t*>(args.C) + (size_t)(row0 + grow) * N + n0 + part * 32;
+          *reinterpret_cast<v4i*>(C) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+          *reinterpret_cast<v4i*>(C + 16) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+          if (part == 0) args.sC[(size_t)(row0 + grow) * (N / 128) + n0 / 128] = sc;
+        }
+        if (NPASS > 1) __syncthreads();
       }
     }
     __syncthreads();  // LDS (row_src, table, stages) is reused by the next tile
@@ -753,14 +779,17 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
 }
 
 // Grid and template instance of one grouped GEMM launch (the instances a launcher
-// uses are compiled in its own source file).
+// uses are compiled in its own source file).  bmb: rows of the large-group tiles, 128 or
+// (e4m3 weights, K <= 128 * kGemmMaxKBlocks192) 192.
 template <bool W4>
 hipError_t launch_gemm_impl(const uint8_t* A, const float* sA, const int32_t* a_rows,
                             int a_row_div, const uint8_t* Bf, const float* sB,
                             const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
                             void* C, float* sC, int bm, int num_cus, hipStream_t s,
-                            int rows_mode, int cap, int big_rpr = -1) {
+                            int rows_mode, int cap, int big_rpr = -1, int bmb = 128) {
   if (K / 128 > kGemmMaxKBlocks) return hipErrorInvalidValue;
+  if (bmb != 128 && (bmb != 192 || W4 || K / 128 > kGemmMaxKBlocks192))
+    return hipErrorInvalidValue;
   GemmArgs a{A, sA, a_rows, a_row_div, Bf, offsets, G, N, K, C, sC, rows_mode, cap,
              W4 ? sB : nullptr, big_rpr};
   const long tiles_n = swiglu ? N / 128 : (N + 255) / 256;
@@ -769,11 +798,21 @@ hipError_t launch_gemm_impl(const uint8_t* A, const float* sA, const int32_t* a_
   if (grid >= 8) grid = grid / 8 * 8;
   if (grid < 1) grid = 1;
   dim3 gd((unsigned)grid), bd(512);
-  // bm: tile rows of small groups (16, 32 or 64); larger groups use 128-row tiles.  The
-  // 4-bit path has no 64-row instance (its register budget); 64 means 32 there.
+  // bm: tile rows of small groups (16, 32 or 64); larger groups use bmb-row tiles.  The
+  // 4-bit path has no 64-row instance (its register budget); 64 means 32 there.  192-row
+  // tiles pair with 16- and 32-row small tiles only (with 64 the instance spills), so
+  // bm = 64 keeps 128-row tiles.
   const int bms = bm >= 64 ? (W4 ? 32 : 64) : bm;
-#define MOE_GEMM_CASE(BMSV, SW) \
-  hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, SW, W4>), gd, bd, 0, s, a, sB)
+#define MOE_GEMM_CASE(BMSV, SW)                                                            \
+  do {                                                                                     \
+    if constexpr (!W4 && BMSV <= 32) {                                                     \
+      if (bmb == 192) {                                                                    \
+        hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, SW, false, 192>), gd, bd, 0, s, a, sB);  \
+        break;                                                                             \
+      }                                                                                    \
+    }                                                                                      \
+    hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, SW, W4, 128>), gd, bd, 0, s, a, sB);         \
+  } while (0)
   if (swiglu) {
     switch (bms) {
       case 16: MOE_GEMM_CASE(16, true); break;

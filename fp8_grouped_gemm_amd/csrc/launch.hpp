@@ -35,6 +35,8 @@ hipError_t launch_quant_weight_int4(const float* w, int G, int N, int K, uint8_t
                                     hipStream_t s);
 // The FP8 GEMM keeps a tile's activation scales for every K block in LDS: K <= 128 * this.
 constexpr int kGemmMaxKBlocks = 128;
+// ... and its 192-row tiles (three stages of 24 KB beside the table) for K <= 128 * this
+constexpr int kGemmMaxKBlocks192 = 64;
 // B [G][R][K] e4m3 -> the fragment-major layout the FP8 GEMM reads (same byte count)
 hipError_t launch_pack_weight_fp8(const uint8_t* B, int G, int R, int K, uint8_t* Bf,
                                   hipStream_t s);
