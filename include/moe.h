@@ -228,7 +228,12 @@ int moe_quant_weight_int4(const float *w, int G, int N, int K, uint8_t *q, float
  * gemm_fp8, the layer's row bound per expert in moe_layer_fwd) with K / 128 even have
  * their whole 256-row tiles computed by a 256 x 256-tile kernel launched first on the
  * same stream; the definition above holds either way (the same promotion order, so
- * bit-identical outputs in every tested case).  Unset or any other value: one kernel. */
+ * bit-identical outputs in every tested case).  Unset or any other value: one kernel.
+ * Groups above the small-tile size are cut into 192-row tiles when K <= 8192 (into
+ * 128-row tiles for larger K and with FP8GG_BIG_TILES; gemm_fp8 takes whichever of the two
+ * gives its M the shorter schedule); FP8GG_TILE_ROWS=128 or 192 in the environment (read
+ * at each call) forces one where both are possible.  Every choice computes each output
+ * with the same block products and promotion order: bit-identical results. */
 int grouped_gemm_fp8(const uint8_t *A, const float *sA, const int32_t *a_rows, int a_row_div,
                      const uint8_t *B, const float *sB, const int32_t *offsets, int G,
                      int R_cap, int N, int K, int epilogue, moe_dtype out_dt, void *C,
