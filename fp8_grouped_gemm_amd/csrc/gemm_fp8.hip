@@ -10,7 +10,8 @@ namespace moe {
 
 // Rows of the large-group tiles.  192-row tiles move 22% fewer operand bytes per FLOP
 // than 128-row ones and measured faster wherever groups are tiled (Zipf grouped GEMM
-// +3-5%, prefill layer 1-2%, bit-identical results); a dense M is tiled by whichever
+// +3-5%, prefill layer 1-2%, the 4-bit-weight hash layer 6%: its ~128-row experts fit one
+// tile; bit-identical results); a dense M is tiled by whichever
 // size gives the shorter schedule: rounds of the grid times the tile's cost (a 192-row
 // tile measured at ~1.37 times a 128-row one), so M = 8192 (four full rounds of 128-row
 // tiles) keeps 128.  K above 128 * kGemmMaxKBlocks192 and the opt-in 256-row mode keep

@@ -68,7 +68,8 @@ hipError_t launch_gemm_w4a8(const uint8_t* A, const float* sA, const int32_t* a_
                             void* C, float* sC, int bm, int num_cus, hipStream_t s, int rows_mode,
                             int cap) {
   return launch_gemm_impl<true>(A, sA, a_rows, a_row_div, Bf, s7f, offsets, G, R_cap, N, K,
-                                swiglu, C, sC, bm, num_cus, s, rows_mode, cap);
+                                swiglu, C, sC, bm, num_cus, s, rows_mode, cap, -1,
+                                large_tile_rows(rows_mode, cap, N, K, swiglu, num_cus, false));
 }
 
 }  // namespace moe

@@ -50,6 +50,8 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const float* sA, const int32_t* a_r
                            const int32_t* offsets, int G, int R_cap, int N, int K, bool swiglu,
                            void* C, float* sC, int bm, int num_cus, hipStream_t s,
                            int rows_mode = 0, int cap = 0, bool big = false);
+// rows of the FP8 GEMM's large-group tiles (128 or 192) for a launch (gemm_fp8.hip)
+int large_tile_rows(int rows_mode, int M, int N, int K, bool swiglu, int num_cus, bool big);
 // the 256 x 256-tile kernel alone, and its row tiles per round (the cut both launches use)
 int big_rows_per_round(int N, bool swiglu, int num_cus);
 hipError_t launch_gemm_fp8_big(const uint8_t* A, const float* sA, const int32_t* a_rows,

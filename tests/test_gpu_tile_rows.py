@@ -137,3 +137,15 @@ def test_tile_rows_dense(Mrows, monkeypatch):
     qb, sb = M.moe_quant_weight_fp8(b.to(dev()))
     qbp = M.moe_pack_weight_fp8(qb)
     _both(monkeypatch, lambda: M.gemm_fp8(qa, sa, qbp[0], sb[0]))
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_tile_rows_w4a8(swiglu, monkeypatch):
+    """The 4-bit-weight instance in both tile sizes (hash-layer-like groups of ~128 rows)."""
+    note(f"tile rows w4a8 swiglu={swiglu}")
+    sizes, N, K = [120, 150, 0, 131, 193, 17], 256, 2048
+    a, b, qa, sa, _, _, offsets, R = _case(sizes, N, K, 16, 25, swiglu)
+    qf, s7f = M.moe_pack_weight_int4(*M.moe_quant_weight_int4(b.to(dev())))
+    off_d = torch.from_numpy(offsets).to(dev())
+    _both(monkeypatch,
+          lambda: M.grouped_gemm_w4a8(qa, sa, qf, s7f, off_d, R, N, swiglu=swiglu))
