@@ -299,6 +299,10 @@ def main(argv=None):
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="print per-kernel average counter values of a rocprofv3 --pmc "
                          "--output-format csv run written to DIR, then exit")
+    ap.add_argument("--counters-md", nargs=5, metavar=("P1", "P2", "P3", "FETCH_DIR", "WRITE_DIR"),
+                    help="print the markdown counter summary of the FP8 GEMM kernels of --workload "
+                         "from the three COUNTER_PASSES runs and a FETCH_SIZE / WRITE_SIZE pair, "
+                         "then exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print HBM bytes per dispatch of the GEMM kernels from a FETCH_SIZE "
                          "and a WRITE_SIZE rocprofv3 --pmc run of --workload (prefill_fp8, decode_fp8 or "
@@ -309,6 +313,9 @@ def main(argv=None):
         return 0
     if a.pmc_summary:
         print(json.dumps(pmc_summary(a.pmc_summary), indent=1))
+        return 0
+    if a.counters_md:
+        print(counters_md(a.workload, a.counters_md[:3], *a.counters_md[3:]))
         return 0
     if a.traffic_summary:
         print(json.dumps(traffic_summary(*a.traffic_summary, a.workload), indent=1))
@@ -545,6 +552,79 @@ TRAFFIC_FILES = {"prefill_fp8": "gemm_fp8_prefill_traffic.json",
                  "decode_fp8": "gemm_fp8_decode_traffic.json",
                  "grouped_gemm_fp8": "grouped_gemm_fp8_traffic.json"}
 CALIB_KERNEL = "moe::quant_weight_fp8_kernel"
+
+
+# the counter sets of the GEMM counter summaries, one rocprofv3 --pmc run each (within the
+# per-run limits: at most 8 SQ, 4 TCC, 4 TCP, 2 TA and 2 GRBM counters)
+COUNTER_PASSES = [
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS "
+    "SQ_LDS_BANK_CONFLICT SQ_INSTS_MFMA GRBM_GUI_ACTIVE",
+    "SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_ANY SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_ANY",
+    "TA_BUSY_avr TA_BUSY_max TCP_PENDING_STALL_CYCLES_sum TCP_TCR_TCP_STALL_CYCLES_sum "
+    "SQ_INSTS_VMEM_RD SQ_INSTS_VALU SQ_INSTS_SALU GRBM_COUNT",
+]
+# bytes the roofline credits per launch of each GEMM role (weights and scales; the
+# standalone GEMM: its operands and output)
+CREDITED_BYTES = {"prefill_fp8": {"gemm1": 7518027776, "gemm2": 3759013888},
+                  "grouped_gemm_fp8": {"gemm": 615493632}}
+
+
+def counters_md(workload, pass_dirs, fetch_dir, write_dir, num_cus=256):
+    """Markdown summary of the FP8 GEMM kernels' hardware counters: the three
+    COUNTER_PASSES runs and the FETCH_SIZE / WRITE_SIZE pair of `workload`, averaged per
+    dispatch, with the derived ratios (GRBM_GUI_ACTIVE summed over the 8 XCDs: / 8 is the
+    kernel's length in shader cycles)."""
+    merged = {}
+    for d in list(pass_dirs) + [fetch_dir, write_dir]:
+        for k, cs in pmc_summary(d).items():
+            if "gemm_fp8_kernel" in k:
+                merged.setdefault(k, {}).update(cs)
+    tr = traffic_summary(fetch_dir, write_dir, workload)
+    roles = {v["kernel"]: r for r, v in tr["roles"].items()}
+    out = []
+    for k, cs in merged.items():
+        v = {c: x["avg"] for c, x in cs.items()}
+        cyc = v["GRBM_GUI_ACTIVE"] / 8
+        role = roles.get(k, "")
+        rows = [
+            ("MFMA pipe busy", f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x {num_cus} CU x 4 SIMD)",
+             v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * num_cus * 4)),
+            ("TA busy", "TA_BUSY_avr / (GRBM_GUI_ACTIVE/8)", v["TA_BUSY_avr"] / cyc),
+            ("TCP pending-request stall", f"TCP_PENDING_STALL_CYCLES_sum / ({num_cus} x GRBM_GUI_ACTIVE/8)",
+             v["TCP_PENDING_STALL_CYCLES_sum"] / (num_cus * cyc)),
+            ("wave time in s_waitcnt", "SQ_WAIT_ANY / SQ_WAVE_CYCLES", v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"]),
+            ("wave time waiting to issue", "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+             v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"]),
+            ("VALU-active wave time", "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES",
+             v["SQ_ACTIVE_INST_VALU"] / v["SQ_WAVE_CYCLES"]),
+            ("LDS bank-conflict share", "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+             v["SQ_LDS_BANK_CONFLICT"] / v["SQ_LDS_IDX_ACTIVE"]),
+            ("MFMA instructions per LDS instruction", "SQ_INSTS_MFMA / SQ_INSTS_LDS",
+             v["SQ_INSTS_MFMA"] / v["SQ_INSTS_LDS"]),
+        ]
+        out += [f"## `{k}` ({role or 'kernel'})", "", "| derived | formula | value |", "|---|---|---|"]
+        out += [f"| {n} | {f} | {x:.3f} |" for n, f, x in rows]
+        if k in tr["kernels"]:
+            hb = tr["kernels"][k]["hbm_bytes_per_launch"]
+            cal = tr["calibration"]
+            cred = CREDITED_BYTES.get(workload, {}).get(role)
+            extra = f" ({hb / cred:.2f}x the {cred / 1e9:.3f} GB credited)" if cred else ""
+            out.append(f"| HBM-side bytes per launch | FETCH_SIZE x {cal['fetch_factor']:.4f} + "
+                       f"WRITE_SIZE x {cal['write_factor']:.4f} (KiB) | {hb / 1e9:.3f} GB{extra} |")
+        out += ["", "| counter | average per dispatch | dispatches |", "|---|---|---|"]
+        out += [f"| {c} | {cs[c]['avg']:.6g} | {cs[c]['dispatches']} |" for c in sorted(cs)]
+        out.append("")
+    cal = tr["calibration"]
+    out.append(f"Calibration of the traffic counters: `{cal['kernel']}` in the same runs reads "
+               f"{cal['known_read_bytes_per_dispatch']:.0f} B and writes "
+               f"{cal['known_write_bytes_per_dispatch']:.0f} B per dispatch (fp32 in, e4m3 codes and "
+               f"block scales out); FETCH_SIZE read {cal['fetch_kib']:.1f} KiB (factor "
+               f"{cal['fetch_factor']:.4f}), WRITE_SIZE {cal['write_kib']:.1f} KiB (factor "
+               f"{cal['write_factor']:.4f}).  FETCH_SIZE counts L2 fills from the fabric, so "
+               f"last-level (MALL) cache hits are included.  GEMM sources sha256 "
+               f"{tr['gemm_source_sha256'][:16]}.")
+    return "\n".join(out)
 
 
 def traffic_summary(fetch_dir, write_dir, workload):
