@@ -21,20 +21,25 @@
 //     while the other wave's MFMAs occupy the matrix core.  A workgroup tile is BM rows x
 //     256 weight rows (plain: 256 output columns; SwiGLU: 128 gate + 128 up rows, so the
 //     1x128 requant block is complete in one workgroup).  The waves split the weight rows
-//     (32 each) and all share the BM activation rows.
+//     (32 each) and all share the BM activation rows.  Large groups use BMB = 128 or 192
+//     rows per tile (two instances; the launcher picks one per launch): a 192-row tile
+//     moves 22% fewer operand bytes per FLOP, and fits the 256 registers a wave has at two
+//     waves per SIMD with one fragment step of read-ahead, a two-block weight ring and
+//     three activation stages, its epilogue staged in two 96-row passes.
 //   * Weights are stored fragment-major (moe_pack_weight_fp8): the 2 KB a wave needs
 //     for one 16-row x 128-deep fragment are contiguous, in the order the MFMA takes
 //     them, and go straight from memory to registers -- no LDS traffic, fully coalesced
-//     loads, three K blocks in flight per wave.
+//     loads, three K blocks in flight per wave (two in 192-row tiles, six in small ones).
 //   * Activation rows (gathered through a_rows) reach LDS by direct global->LDS DMA into
-//     four stages, in a 16-byte XOR swizzle read back without bank conflicts.  One
-//     barrier per K block, placed two fragment steps before the block ends; the reads
-//     of those last steps already fetch the next block's first fragments, so the MFMAs
-//     never wait on the barrier.
+//     four stages (three in 192-row tiles), in a 16-byte XOR swizzle read back without
+//     bank conflicts.  One barrier per K block, placed two fragment steps (192-row
+//     tiles: one) before the block ends; the reads of those last steps already fetch the
+//     next block's first fragments, so the MFMAs never wait on the barrier.
 //   * The tile's activation scales for all K blocks are transposed into LDS once per
-//     tile, so that the K loop loads no scattered scale words; for 128-row tiles with
-//     K <= 8192 the table holds the products sA*sB (one table per weight-scale block of
-//     the tile), so the promotion needs no multiply in the K loop.
+//     tile, so that the K loop loads no scattered scale words; for large tiles with
+//     K <= 8192 (192-row tiles: K <= 4096) the table holds the products sA*sB (one table
+//     per weight-scale block of the tile), so the promotion needs no multiply in the K
+//     loop.
 //   * Persistent grid; workgroup b works on tiles v, v+P, ... with v = (b mod 8) * P/8 +
 //     b/8, so that the 32 tiles one XCD holds at a time are consecutive; inside a group
 //     they run down up to 16 row tiles before moving to the next column tile, so those
@@ -133,8 +138,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
   // epilogue rows of 528 bytes (192-row tiles: staged in two passes of 96 rows)
   constexpr int OUT_FLOATS = (BMB > 128 ? BMB / 2 : BMB) * 132;
   __shared__ TileMap tm;
-  // four activation stages, each an LDS object of its own (see dma16b); the row-scale
-  // table [kb][row] doubles as the epilogue's staging area
+  // NSA activation stages, each an LDS object of its own (see dma16b; st3 is unused with
+  // three); the row-scale table [kb][row] doubles as the epilogue's staging area
   __shared__ __attribute__((aligned(1024))) uint8_t st0[A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[A_STAGE];
