@@ -705,14 +705,20 @@ int layer_front(const moe_layer_desc* d, const moe_layer_weights* w, const void*
   }
   const int cap = moe_capacity(T, k, E, d->capacity_factor);
   if (cap < 0) return cap;
+  if (!masked && (d->mode == MOE_MODE_FP8 || d->mode == MOE_MODE_W4A8)) {
+    // the per-token quantisation does not depend on the routing: it runs in the dispatch
+    // launch, beside the one workgroup that dispatches
+    STEP(moe::launch_dispatch_quant(P.idx, T, k, E, d->m_align, cap, P.counts, P.offsets,
+                                    P.ros, P.sor, R, x, D, P.qx, P.sx, s),
+         "dispatch and quant launch");
+    return MOE_OK;
+  }
   STEP(moe::launch_dispatch(P.idx, T, k, E, d->m_align, cap, P.counts,
                             masked ? nullptr : P.offsets, P.ros, P.sor, R, s, masked),
        "dispatch launch");
   if (d->mode == MOE_MODE_FP8 && masked) {
     // fixed-capacity layout: token codes gathered into [E, C, d], empty rows zero
     STEP(moe::launch_quant_act(x, true, D, P.sor, k, R, P.qx, P.sx, s), "quant-gather launch");
-  } else if (d->mode == MOE_MODE_FP8 || d->mode == MOE_MODE_W4A8) {
-    STEP(moe::launch_quant_act(x, true, D, nullptr, 1, T, P.qx, P.sx, s), "quant launch");
   }
   return MOE_OK;
 }

@@ -13,6 +13,7 @@
 // above that, one workgroup per expert scans the whole slot list.
 #include "common.hpp"
 #include "launch.hpp"
+#include "quant_act.hpp"
 
 namespace moe {
 
@@ -103,11 +104,33 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 // at a time: a 64-bit mask per expert marks the lanes that chose it, so a slot's rank
 // among them is the popcount of the mask below its lane, and the lowest such lane
 // advances the expert's row.  Slot order inside every expert is thus preserved.
-template <int EMAX>
+//
+// QX: workgroups 1.. quantise the token rows (bf16 x [T, K] -> 1x128 e4m3 codes and
+// scales, 64 blocks of 128 per workgroup) while workgroup 0 dispatches: the quantisation
+// does not depend on the routing, and the dispatch alone occupies one CU.
+struct QuantRows {
+  const void* x;
+  int K, rows;
+  uint8_t* q;
+  float* scales;
+};
+
+template <int EMAX, bool QX = false>
 __global__ __launch_bounds__(1024) void dispatch_fused_kernel(
     const int32_t* __restrict__ idx, int n_slots, int E, int m_align, int cap, bool fixed,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_of_slot, int32_t* __restrict__ slot_of_row, int rows_bound) {
+    int32_t* __restrict__ row_of_slot, int32_t* __restrict__ slot_of_row, int rows_bound,
+    QuantRows qr = {}) {
+  if constexpr (QX) {
+    if (blockIdx.x > 0) {
+      const int KB = qr.K / 128;
+      const long g = ((long)(blockIdx.x - 1) * 1024 + threadIdx.x) >> 4;
+      if (g >= (long)qr.rows * KB) return;     // whole 16-lane groups exit together
+      const int row = (int)(g / KB), kb = (int)(g % KB);
+      quant_act_block<true>(qr.x, qr.K, row, row, kb, threadIdx.x & 15, qr.q, qr.scales);
+      return;
+    }
+  }
   constexpr int NW = 16;
   __shared__ int cnt[NW][EMAX];                    // counts, then running row of the segment
   __shared__ unsigned long long msk[NW][EMAX];
@@ -211,6 +234,29 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int m_align,
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(E), dim3(256), 0, s, idx, n, E, m_align, cap,
                      fixed, counts, offsets, row_of_slot, slot_of_row, rows_bound);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_quant(const int32_t* idx, int T, int k, int E, int m_align, int cap,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                                 int32_t* slot_of_row, int rows_bound, const void* x, int K,
+                                 uint8_t* q, float* scales, hipStream_t s) {
+  if (E > 512 || T == 0) {
+    hipError_t err = launch_dispatch(idx, T, k, E, m_align, cap, counts, offsets, row_of_slot,
+                                     slot_of_row, rows_bound, s);
+    if (err != hipSuccess) return err;
+    return launch_quant_act(x, true, K, nullptr, 1, T, q, scales, s);
+  }
+  const QuantRows qr{x, K, T, q, scales};
+  const long qblocks = ((long)T * (K / 128) * 16 + 1023) / 1024;
+  const dim3 grid((unsigned)(1 + qblocks)), block(1024);
+  const int n = T * k;
+  if (E <= 256)
+    hipLaunchKernelGGL((dispatch_fused_kernel<256, true>), grid, block, 0, s, idx, n, E, m_align,
+                       cap, false, counts, offsets, row_of_slot, slot_of_row, rows_bound, qr);
+  else
+    hipLaunchKernelGGL((dispatch_fused_kernel<512, true>), grid, block, 0, s, idx, n, E, m_align,
+                       cap, false, counts, offsets, row_of_slot, slot_of_row, rows_bound, qr);
   return hipGetLastError();
 }
 

@@ -25,6 +25,13 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int m_align,
                            int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
                            int32_t* slot_of_row, int rows_bound, hipStream_t s,
                            bool fixed = false);
+// launch_dispatch (contiguous layout) and launch_quant_act of bf16 x [T, K] (no gather) in
+// one launch: one workgroup dispatches while the others quantise (E <= 512; above that
+// the two launches)
+hipError_t launch_dispatch_quant(const int32_t* idx, int T, int k, int E, int m_align, int cap,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                                 int32_t* slot_of_row, int rows_bound, const void* x, int K,
+                                 uint8_t* q, float* scales, hipStream_t s);
 // p[0..n) = v
 hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);
 hipError_t launch_quant_act(const void* x, bool bf16, int K, const int32_t* src_row, int src_div,

@@ -8,6 +8,7 @@
 // lecture, tqpw.cn sec. 3.1).
 #include "common.hpp"
 #include "launch.hpp"
+#include "quant_act.hpp"
 
 namespace moe {
 
@@ -28,38 +29,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
     int sr = src_row[row];
     src = sr < 0 ? -1 : sr / src_div;
   }
-  float v[8];
-  if (src < 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  } else if (BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(x) + (size_t)src * K + kb * 128 + li * 8;
-    v4i raw = *reinterpret_cast<const v4i*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_to_f32((uint16_t)(raw[i] & 0xFFFF));
-      v[2 * i + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[i] >> 16));
-    }
-  } else {
-    const float* p = static_cast<const float*>(x) + (size_t)src * K + kb * 128 + li * 8;
-    v4f a = *reinterpret_cast<const v4f*>(p);
-    v4f b = *reinterpret_cast<const v4f*>(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = group_max<16>(amax);
-  const float s = block_scale(amax);
-  uint32_t lo = e4m3x4(clamp448(v[0] / s), clamp448(v[1] / s), clamp448(v[2] / s),
-                       clamp448(v[3] / s));
-  uint32_t hi = e4m3x4(clamp448(v[4] / s), clamp448(v[5] / s), clamp448(v[6] / s),
-                       clamp448(v[7] / s));
-  uint32_t* qp = reinterpret_cast<uint32_t*>(q + (size_t)row * K + kb * 128 + li * 8);
-  qp[0] = lo;
-  qp[1] = hi;
-  if (li == 0) scales[(size_t)row * KB + kb] = s;
+  quant_act_block<BF16>(x, K, src, row, kb, li, q, scales);
 }
 
 // One workgroup per 128x128 block: thread t owns row t/2, 64 consecutive elements.
