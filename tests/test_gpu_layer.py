@@ -180,6 +180,15 @@ def test_layer_no_tokens(mode):
     assert torch.equal(counts.cpu(), torch.zeros(w.E, dtype=torch.int32))
 
 
+@pytest.mark.parametrize("E", [300, 520])
+def test_layer_fp8_wide_expert_counts(E):
+    """Expert counts past the 256-expert dispatch instance: the 512-expert one (its
+    workgroups 1.. quantising the tokens) and the separate count/scatter launches above
+    512 experts, with most experts empty."""
+    run_layer_case(synth.Workload(f"wide_e{E}", T=64, d=256, E=E, k=4, I=256, mode="fp8",
+                                  m_align=16, seed=6))
+
+
 def test_layer_small_fp8_many_experts():
     run_layer_case(synth.Workload("small_fp8_e64", T=200, d=384, E=64, k=6, I=128, mode="fp8",
                                   m_align=32, seed=3))
