@@ -122,7 +122,7 @@ __device__ __forceinline__ v8i expand_int4_e4m3(v4i w) {
 template <int BMS, bool SWIGLU, bool W4 = false, int BMB = 128>
 __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
                                                            const float* __restrict__ sB) {
-  static_assert(BMB == 128 || BMB == 192, "large-tile rows");
+  static_assert(BMB == 128 || BMB == 160 || BMB == 192, "large-tile rows");
   constexpr int NW = 8, NT = 512, TN = 2;
   constexpr int BN_OUT = SWIGLU ? 128 : 256;       // output columns per tile
   constexpr int WB = (SWIGLU ? 128 : 256) / NW;    // weight rows per wave (per half: SwiGLU)
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
     // slot L%8 and fetches global piece (L%8) ^ swz(row).  Every wave issues ADMA
     // instructions per block (small tiles repeat row groups, same bytes to same place).
     constexpr int GROUPS = BM / 8;
-    constexpr int ADMA = GROUPS > NW ? GROUPS / NW : 1;
+    constexpr int ADMA = GROUPS > NW ? (GROUPS + NW - 1) / NW : 1;  // (160 rows: 20 groups)
     uint32_t a_voff[ADMA], a_m[ADMA];
 #pragma unroll
     for (int q = 0; q < ADMA; ++q) {
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(GemmArgs args,
 
 // Grid and template instance of one grouped GEMM launch (the instances a launcher
 // uses are compiled in its own source file).  bmb: rows of the large-group tiles, 128 or
-// (K <= 128 * kGemmMaxKBlocks192) 192.
+// (K <= 128 * kGemmMaxKBlocks192) 192, or (4-bit weights) 160.
 template <bool W4>
 hipError_t launch_gemm_impl(const uint8_t* A, const float* sA, const int32_t* a_rows,
                             int a_row_div, const uint8_t* Bf, const float* sB,
@@ -793,7 +793,7 @@ hipError_t launch_gemm_impl(const uint8_t* A, const float* sA, const int32_t* a_
                             void* C, float* sC, int bm, int num_cus, hipStream_t s,
                             int rows_mode, int cap, int big_rpr = -1, int bmb = 128) {
   if (K / 128 > kGemmMaxKBlocks) return hipErrorInvalidValue;
-  if (bmb != 128 && (bmb != 192 || K / 128 > kGemmMaxKBlocks192))
+  if (bmb != 128 && ((bmb != 192 && (bmb != 160 || !W4)) || K / 128 > kGemmMaxKBlocks192))
     return hipErrorInvalidValue;
   GemmArgs a{A, sA, a_rows, a_row_div, Bf, offsets, G, N, K, C, sC, rows_mode, cap,
              W4 ? sB : nullptr, big_rpr};
@@ -814,6 +814,12 @@ hipError_t launch_gemm_impl(const uint8_t* A, const float* sA, const int32_t* a_
       if (bmb == 192) {                                                                    \
         hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, SW, W4, 192>), gd, bd, 0, s, a, sB);     \
         break;                                                                             \
+      }                                                                                    \
+      if constexpr (W4) {                                                                  \
+        if (bmb == 160) {                                                                  \
+          hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, SW, W4, 160>), gd, bd, 0, s, a, sB);   \
+          break;                                                                           \
+        }                                                                                  \
       }                                                                                    \
     }                                                                                      \
     hipLaunchKernelGGL((gemm_fp8_kernel<BMSV, SW, W4, 128>), gd, bd, 0, s, a, sB);         \

@@ -29,11 +29,11 @@ def _case(sizes, N, K, m_align, seed, swiglu):
     return a, b, qa, sa, qb, sb, offsets, R
 
 
-def _both(monkeypatch, fn, rows=None):
-    """fn() under FP8GG_TILE_ROWS=128, =192 and unset: equal bit for bit (on the output
-    rows a call writes: all, or the boolean mask ``rows``)."""
+def _both(monkeypatch, fn, rows=None, heights=("128", "192")):
+    """fn() under each FP8GG_TILE_ROWS value in ``heights`` and unset: equal bit for bit
+    (on the output rows a call writes: all, or the boolean mask ``rows``)."""
     out = {}
-    for tr in ("128", "192"):
+    for tr in heights:
         monkeypatch.setenv("FP8GG_TILE_ROWS", tr)
         r = fn()
         torch.cuda.synchronize()
@@ -42,13 +42,13 @@ def _both(monkeypatch, fn, rows=None):
     d = fn()
     torch.cuda.synchronize()
     out["default"] = [t.clone() for t in (d if isinstance(d, tuple) else (d,))]
-    for x, y, z in zip(out["128"], out["192"], out["default"]):
-        if rows is not None:
-            keep = torch.from_numpy(rows).to(x.device)
-            x, y, z = x[keep], y[keep], z[keep]
-        assert torch.equal(x, y)
-        assert torch.equal(x, z)
-    return out["128"]
+    keep = torch.from_numpy(rows).to(dev()) if rows is not None else None
+    for tr in list(heights[1:]) + ["default"]:
+        for x, y in zip(out[heights[0]], out[tr]):
+            if keep is not None:
+                x, y = x[keep], y[keep]
+            assert torch.equal(x, y), tr
+    return out[heights[0]]
 
 
 @pytest.mark.parametrize("sizes,m_align,K", [
@@ -141,11 +141,13 @@ def test_tile_rows_dense(Mrows, monkeypatch):
 
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_tile_rows_w4a8(swiglu, monkeypatch):
-    """The 4-bit-weight instance in both tile sizes (hash-layer-like groups of ~128 rows)."""
+    """The 4-bit-weight instance in its three tile heights (hash-layer-like groups of ~128
+    rows, one of 193)."""
     note(f"tile rows w4a8 swiglu={swiglu}")
     sizes, N, K = [120, 150, 0, 131, 193, 17], 256, 2048
     a, b, qa, sa, _, _, offsets, R = _case(sizes, N, K, 16, 25, swiglu)
     qf, s7f = M.moe_pack_weight_int4(*M.moe_quant_weight_int4(b.to(dev())))
     off_d = torch.from_numpy(offsets).to(dev())
     _both(monkeypatch,
-          lambda: M.grouped_gemm_w4a8(qa, sa, qf, s7f, off_d, R, N, swiglu=swiglu))
+          lambda: M.grouped_gemm_w4a8(qa, sa, qf, s7f, off_d, R, N, swiglu=swiglu),
+          heights=("128", "160", "192"))
