@@ -277,7 +277,9 @@ int moe_pack_weight_int4(const uint8_t *q, const float *s7, int G, int N, int K,
  * are exact; the activations are 1x128 e4m3 as in grouped_gemm_fp8.  Each 128-deep block
  * is promoted as acc += sA[a, kb] * s7[g, n, kb] * partial (two-level accumulation,
  * qidao123.com day 3).  B and s7 as packed by moe_pack_weight_int4 ([G, Nb, K] logical,
- * Nb = N or 2N for SwiGLU); every other argument, output and limit as grouped_gemm_fp8. */
+ * Nb = N or 2N for SwiGLU); every other argument, output and limit as grouped_gemm_fp8.
+ * Kernel choice as grouped_gemm_fp8, except that groups of at most ~170 rows (R_cap / G)
+ * are cut into 160-row tiles (FP8GG_TILE_ROWS=160 forces them): bit-identical results. */
 int grouped_gemm_w4a8(const uint8_t *A, const float *sA, const int32_t *a_rows, int a_row_div,
                       const uint8_t *B, const float *s7, const int32_t *offsets, int G,
                       int R_cap, int N, int K, int epilogue, moe_dtype out_dt, void *C,
